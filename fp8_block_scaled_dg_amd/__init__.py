@@ -1,0 +1,218 @@
+"""MI355X (gfx950) FP8 E4M3 block-scaled GEMM: Python binding of libdg.so.
+
+Argument marshalling only: every step runs in the HIP kernels of libdg.so
+(declared in include/dg.h).  PyTorch provides device memory and the current
+stream.  There is no fallback: if the library is missing or fails to load,
+importing this package raises.
+
+Entry points (same names as the C ABI):
+    dg_quantize_fp8_block(q, scales, x, block_rows)
+    dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, workspace=None)
+    dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows, m_indices)
+Conveniences mirroring the DeepGEMM page's Python API (pzsr.cn, s4.1):
+    to_fp8(x, block_rows=128) -> (q, scales)
+    fp8_gemm_nt(c, a, b, sa, sb, a_block_rows=128)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libdg.so")
+
+DG_OK = 0
+ABI_VERSION = 1
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libdg.so not built (%s); run `python -m fp8_block_scaled_dg_amd.build`"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.dg_abi_version.restype = i32
+    lib.dg_abi_version.argtypes = []
+    lib.dg_status_string.restype = ctypes.c_char_p
+    lib.dg_status_string.argtypes = [i32]
+    lib.dg_get_mk_alignment_for_contiguous_layout.restype = i32
+    lib.dg_get_mk_alignment_for_contiguous_layout.argtypes = []
+    lib.dg_quantize_fp8_block.restype = i32
+    lib.dg_quantize_fp8_block.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    lib.dg_fp8_gemm_nt_workspace_bytes.restype = ctypes.c_size_t
+    lib.dg_fp8_gemm_nt_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.dg_fp8_gemm_nt.restype = i32
+    lib.dg_fp8_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.dg_fp8_grouped_gemm_contig.restype = i32
+    lib.dg_fp8_grouped_gemm_contig.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
+    if lib.dg_abi_version() != ABI_VERSION:
+        raise ImportError("libdg ABI %d != binding ABI %d" % (lib.dg_abi_version(), ABI_VERSION))
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.dg_status_string(status).decode()
+
+
+def get_mk_alignment_for_contiguous_layout() -> int:
+    return lib.dg_get_mk_alignment_for_contiguous_layout()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream)
+
+
+def _check(rc: int, where: str):
+    if rc != DG_OK:
+        raise DGError(rc, where)
+
+
+def _require(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _codes(t, name):
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _require(t, torch.uint8, name)
+    return t
+
+
+def _bf16(t, name):
+    if t.dtype in (torch.bfloat16, getattr(torch, "uint16", torch.int16)):
+        t = t.view(torch.int16)
+    _require(t, torch.int16, name)
+    return t
+
+
+def cdiv(a: int, b: int) -> int:
+    return (a + b - 1) // b
+
+
+# ---------------------------------------------------------------------------
+# C-ABI entry points
+# ---------------------------------------------------------------------------
+
+def dg_quantize_fp8_block(q, scales, x, block_rows: int = 128, stream=None) -> None:
+    """x float32 [rows, cols] -> q (uint8/float8_e4m3fn [rows, cols]),
+    scales float32 [ceil(cols/128), ceil(rows/block_rows)]."""
+    _require(x, torch.float32, "x")
+    q = _codes(q, "q")
+    _require(scales, torch.float32, "scales")
+    rows, cols = x.shape
+    if q.shape != x.shape:
+        raise ValueError("q must have the shape of x")
+    if scales.numel() != cdiv(cols, 128) * cdiv(rows, block_rows):
+        raise ValueError("scales must hold ceil(cols/128)*ceil(rows/block_rows) floats")
+    _check(lib.dg_quantize_fp8_block(_ptr(q), _ptr(scales), _ptr(x), rows, cols, block_rows,
+                                     _stream(stream)), "dg_quantize_fp8_block")
+
+
+def dg_fp8_gemm_nt_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+
+
+def dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows: int = 128, workspace=None,
+                   stream=None) -> None:
+    """C[M,N] (bf16) = block-scaled A[M,K] . B[N,K]^T."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sa, torch.float32, "sa")
+    _require(sb, torch.float32, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or c.shape != (M, N):
+        raise ValueError("shape mismatch: a %s, b %s, c %s" % (tuple(a.shape), tuple(b.shape),
+                                                              tuple(c.shape)))
+    if sa.numel() != cdiv(K, 128) * cdiv(M, a_block_rows):
+        raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
+    if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
+    ws_bytes = 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dg_fp8_gemm_nt(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), a_block_rows,
+                              M, N, K, _ptr(workspace), ws_bytes, _stream(stream)),
+           "dg_fp8_gemm_nt")
+
+
+def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices,
+                               stream=None) -> None:
+    """Grouped M-contiguous: a [M,K], b [G,N,K], sb [G,K/128,ceil(N/128)],
+    m_indices int32 [M] (-1 = padding row)."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sa, torch.float32, "sa")
+    _require(sb, torch.float32, "sb")
+    _require(m_indices, torch.int32, "m_indices")
+    M, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K or c.shape != (M, N) or m_indices.shape != (M,):
+        raise ValueError("shape mismatch")
+    if sa.numel() != cdiv(K, 128) * cdiv(M, a_block_rows):
+        raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
+    if sb.numel() != G * cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold G*(K/128)*ceil(N/128) floats")
+    _check(lib.dg_fp8_grouped_gemm_contig(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
+                                          a_block_rows, _ptr(m_indices), G, M, N, K,
+                                          _stream(stream)), "dg_fp8_grouped_gemm_contig")
+
+
+# ---------------------------------------------------------------------------
+# Conveniences (allocate outputs with torch)
+# ---------------------------------------------------------------------------
+
+def to_fp8(x, block_rows: int = 128):
+    """Quantise a float32 device matrix -> (codes uint8 [R, C], scales float32
+    [ceil(C/128), ceil(R/block_rows)])."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty((cdiv(cols, 128), cdiv(rows, block_rows)), dtype=torch.float32,
+                    device=x.device)
+    dg_quantize_fp8_block(q, s, x, block_rows)
+    return q, s
+
+
+def fp8_gemm_nt(c, a, b, sa, sb, a_block_rows: int = 128, workspace=None):
+    dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, workspace)
+    return c
+
+
+def fp8_grouped_gemm_contig(c, a, b, sa, sb, m_indices, a_block_rows: int = 1):
+    dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows, m_indices)
+    return c
+
+
+__all__ = [
+    "lib", "LIB_PATH", "DGError", "status_string", "get_mk_alignment_for_contiguous_layout",
+    "dg_quantize_fp8_block", "dg_fp8_gemm_nt_workspace_bytes", "dg_fp8_gemm_nt",
+    "dg_fp8_grouped_gemm_contig", "to_fp8", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
+]

@@ -1,0 +1,110 @@
+// C ABI of libdg (declared in include/dg.h): host-side validation and
+// dispatch to the gfx950 kernels.  Validation happens before any HIP call, so
+// a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dg.h"
+#include "dg_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kU32 = 4294967295LL;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? DG_OK : DG_ERR_HIP; }
+
+// Checks shared by the dense and grouped GEMMs.
+int check_gemm(const uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
+               const float* sb, int a_block_rows, int64_t M, int64_t N, int64_t K) {
+  if (!c || !a || !b || !sa || !sb) return DG_ERR_NULL;
+  if (a_block_rows != 1 && a_block_rows != 128) return DG_ERR_UNSUPPORTED;
+  if (M < 1 || N < 8 || K < 128) return DG_ERR_SHAPE;
+  if (N % 8 != 0 || K % 128 != 0) return DG_ERR_SHAPE;
+  // 32-bit tile offsets inside the kernels
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return DG_ERR_SHAPE;
+  if (M * K > kU32 || N * K > kU32) return DG_ERR_SHAPE;
+  if (!aligned(c, 16) || !aligned(a, 16) || !aligned(b, 16)) return DG_ERR_ALIGN;
+  if (!aligned(sa, 4) || !aligned(sb, 4)) return DG_ERR_ALIGN;
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_abi_version(void) { return DG_ABI_VERSION; }
+
+const char* dg_status_string(int status) {
+  switch (status) {
+    case DG_OK: return "ok";
+    case DG_ERR_NULL: return "a required pointer is NULL";
+    case DG_ERR_SHAPE: return "invalid or unsupported shape";
+    case DG_ERR_UNSUPPORTED: return "unsupported block_rows or group count";
+    case DG_ERR_ALIGN: return "pointer not suitably aligned";
+    case DG_ERR_WORKSPACE: return "workspace smaller than required";
+    case DG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dg_get_mk_alignment_for_contiguous_layout(void) { return 128; }
+
+int dg_quantize_fp8_block(uint8_t* q, float* scales, const float* x, int64_t rows, int64_t cols,
+                          int block_rows, void* stream) {
+  if (!q || !scales || !x) return DG_ERR_NULL;
+  if (block_rows != 1 && block_rows != 128) return DG_ERR_UNSUPPORTED;
+  if (rows < 1 || cols < 1 || cols % 16 != 0) return DG_ERR_SHAPE;
+  const int64_t n_kb = (cols + 127) / 128;
+  const int64_t grid_y = block_rows == 128 ? (rows + 127) / 128 : (rows + 31) / 32;
+  if (grid_y > kMaxGridY || n_kb > INT32_MAX) return DG_ERR_SHAPE;
+  if (rows > INT64_MAX / cols) return DG_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return DG_ERR_ALIGN;
+  return from_hip(dg::launch_quantize(q, scales, x, rows, cols, block_rows,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  return dg::skinny_applies(M, N, K) ? dg::skinny_workspace_bytes(M, N, K) : 0;
+}
+
+int dg_fp8_gemm_nt(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
+                   const float* sb, int a_block_rows, int64_t M, int64_t N, int64_t K,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
+  if (st != DG_OK) return st;
+  const bool skinny = dg::skinny_applies(M, N, K);
+  if (workspace != nullptr && workspace_bytes > 0) {
+    const size_t need = skinny ? dg::skinny_workspace_bytes(M, N, K) : 0;
+    if (workspace_bytes < need) return DG_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DG_ERR_ALIGN;
+  } else if (workspace != nullptr || workspace_bytes > 0) {
+    workspace = nullptr;  // one of the two missing: treat as "no workspace"
+    workspace_bytes = 0;
+  }
+  dg::GemmProblem p{c, a, b, sa, sb, nullptr, 1, a_block_rows, M, N, K};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (skinny) return from_hip(dg::launch_gemm_skinny(p, workspace, workspace_bytes, s));
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles > INT32_MAX) return DG_ERR_SHAPE;
+  return from_hip(dg::launch_gemm_tiled(p, false, s));
+}
+
+int dg_fp8_grouped_gemm_contig(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
+                               const float* sb, int a_block_rows, const int32_t* m_indices,
+                               int num_groups, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
+  if (st != DG_OK) return st;
+  if (!m_indices) return DG_ERR_NULL;
+  if (!aligned(m_indices, 4)) return DG_ERR_ALIGN;
+  if (num_groups < 1) return DG_ERR_UNSUPPORTED;
+  if (M % 128 != 0) return DG_ERR_SHAPE;
+  if ((int64_t)num_groups * N * K / num_groups != N * K) return DG_ERR_SHAPE;
+  dg::GemmProblem p{c, a, b, sa, sb, m_indices, num_groups, a_block_rows, M, N, K};
+  return from_hip(dg::launch_gemm_tiled(p, true, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

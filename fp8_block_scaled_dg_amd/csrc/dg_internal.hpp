@@ -1,0 +1,35 @@
+// Host-side declarations shared between the C ABI layer and the kernel
+// launchers of libdg (internal; not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dg {
+
+hipError_t launch_quantize(uint8_t* q, float* scales, const float* x, int64_t rows,
+                           int64_t cols, int block_rows, hipStream_t stream);
+
+struct GemmProblem {
+  uint16_t* c;
+  const uint8_t* a;
+  const uint8_t* b;
+  const float* sa;
+  const float* sb;
+  const int32_t* m_indices;  // grouped only, else nullptr
+  int num_groups;            // grouped only, else 1
+  int a_block_rows;          // 1 or 128
+  int64_t M, N, K;
+};
+
+// Large-tile MFMA kernel (dense or grouped).
+hipError_t launch_gemm_tiled(const GemmProblem& p, bool grouped, hipStream_t stream);
+
+// Skinny (small-M) kernel: workspace may be null (then no split-K).
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bool skinny_applies(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_skinny(const GemmProblem& p, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+}  // namespace dg

@@ -1,0 +1,303 @@
+// Tiled FP8 block-scaled NT GEMM for gfx950 (dense and grouped-M).
+//
+// What is computed (FP8 block-quantised GEMM page on lpnh.cn, s2.2 and s3.2;
+// NT layout and grouped MoE GEMM from the DeepGEMM page on pzsr.cn, s3.1-s3.3):
+//   C[m][n] = bf16( sum_kb sa(m,kb) * sb(n,kb) * P_kb[m][n] ),
+//   P_kb[m][n] = sum_{k in 128-wide block kb} A[m][k] * B[n][k]
+// with the E4M3 products summed in FP32 by the matrix cores and promoted into
+// FP32 accumulators once per 128-wide K block.
+//
+// gfx950 mapping
+//  * One v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-wide K block of a
+//    16x16 output sub-tile, so the per-block partial P_kb never needs more
+//    than 4 transient VGPRs: it is produced with a zero accumulator and
+//    immediately folded into the FP32 accumulator with one FMA per element
+//    (acc += P_kb * sa*sb).  The MFMA operands are swapped (B rows feed the
+//    instruction's first operand) so each lane ends up owning 4 consecutive
+//    output columns of one row: one scale per lane and sub-tile row, and
+//    8-byte BF16 stores.
+//  * Workgroup tile BM x 256, K step 128; waves own 64 x 128 sub-tiles
+//    (4 x 8 MFMA tiles, 128 accumulator VGPRs).  BM = 256 -> 8 waves.
+//  * Global -> LDS staging with global_load_lds_dwordx4 (no VGPR round trip),
+//    two LDS stages held in two distinct __shared__ arrays so that the
+//    compiler's LDS-DMA wait tracking can tell the stages apart.
+//  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
+//    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which spreads the 16
+//    rows read by one MFMA fragment load over all banks.  The DMA writes stay
+//    linear (the permutation is applied to the global source addresses).
+//  * Workgroup ids are remapped so that each XCD (ids round-robin over 8
+//    XCDs) works on a contiguous, M-grouped patch of tiles that shares A and
+//    B panels in its own L2.
+#include "dg_device.hpp"
+#include "dg_internal.hpp"
+
+namespace dg {
+namespace {
+
+constexpr int BN = 256;
+constexpr int BK = 128;
+
+struct TiledArgs {
+  uint16_t* c;
+  const uint8_t* a;
+  const uint8_t* b;
+  const float* sa;
+  const float* sb;
+  const int32_t* m_indices;
+  int num_groups;
+  int M, N, K;
+  int nkb;        // K / 128
+  int sa_stride;  // ceil(M / a_block_rows)
+  int sb_stride;  // ceil(N / 128)
+  int tiles_m, tiles_n;
+  int group_m;
+};
+
+__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// Stage one BK-wide slice of a ROWS x 128-byte operand tile into LDS.
+// Wave w issues ITERS instructions; instruction j fills LDS bytes
+// [cb*1024, cb*1024 + 1024) with cb = j*NW + w, i.e. rows cb*8 .. cb*8+7.
+template <int ROWS, int NW>
+struct TileLoader {
+  static constexpr int ITERS = ROWS / 8 / NW;
+  uint32_t off[ITERS];  // byte offset of this lane's source chunk at kb = 0
+
+  __device__ __forceinline__ void init(int wave, int lane, int row0, int rows_valid, int K) {
+#pragma unroll
+    for (int j = 0; j < ITERS; ++j) {
+      const int cb = j * NW + wave;
+      const int r = cb * 8 + (lane >> 3);
+      const int logical = (lane & 7) ^ lds_swz(r);
+      int gr = row0 + r;
+      gr = gr < rows_valid ? gr : rows_valid - 1;  // clamp: rows past the edge only feed
+                                                    // outputs that are never stored
+      off[j] = (uint32_t)gr * (uint32_t)K + (uint32_t)(logical * 16);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint8_t* base, uint8_t* lds, int wave, int kb) const {
+#pragma unroll
+    for (int j = 0; j < ITERS; ++j) {
+      const int cb = j * NW + wave;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(base + off[j] + (uint32_t)kb * BK),
+          (__attribute__((address_space(3))) void*)(lds + cb * 1024), 16, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int off0, int off1) {
+  const v4i lo = *reinterpret_cast<const v4i*>(lds + row_base * 128 + off0);
+  const v4i hi = *reinterpret_cast<const v4i*>(lds + row_base * 128 + off1);
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ void map_tile(const TiledArgs& p, int& tm, int& tn) {
+  int bid = blockIdx.x;
+  const int total = p.tiles_m * p.tiles_n;
+  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int per_group = p.group_m * p.tiles_n;
+  const int group = bid / per_group;
+  const int first_m = group * p.group_m;
+  const int gsz = min(p.tiles_m - first_m, p.group_m);
+  const int rem = bid - group * per_group;
+  tm = first_m + rem % gsz;
+  tn = rem / gsz;
+}
+
+template <int BM, int A_BLK, bool GROUPED>
+__global__ void __launch_bounds__(BM * BN / 128)
+gemm_tiled_kernel(TiledArgs p) {
+  constexpr int WM = BM / 64;
+  constexpr int NW = WM * (BN / 128);
+  constexpr int A_BYTES = BM * BK;
+  constexpr int STAGE = A_BYTES + BN * BK;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+
+  int tm, tn;
+  map_tile(p, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  const uint8_t* bbase = p.b;
+  const float* sbbase = p.sb;
+  if (GROUPED) {
+    const int g = p.m_indices[m0];
+    if (g < 0 || g >= p.num_groups) {
+      // whole block is padding: zero rows
+      for (int idx = threadIdx.x; idx < BM * (BN / 8); idx += NW * 64) {
+        const int r = idx / (BN / 8);
+        const int cc = (idx % (BN / 8)) * 8;
+        if (n0 + cc < p.N)
+          *reinterpret_cast<uint4*>(p.c + (int64_t)(m0 + r) * p.N + n0 + cc) = make_uint4(0, 0, 0, 0);
+      }
+      return;
+    }
+    bbase += (int64_t)g * p.N * p.K;
+    sbbase += (int64_t)g * p.nkb * p.sb_stride;
+  }
+
+  TileLoader<BM, NW> lda;
+  TileLoader<BN, NW> ldb;
+  lda.init(wave, lane, m0, p.M, p.K);
+  ldb.init(wave, lane, n0, p.N, p.K);
+
+  // fragment read offsets (constant per lane: the swizzle depends on r % 16 only)
+  const int fr = lane & 15;
+  const int off0 = fr * 128 + (((2 * (lane >> 4)) ^ lds_swz(fr)) * 16);
+  const int off1 = fr * 128 + (((2 * (lane >> 4) + 1) ^ lds_swz(fr)) * 16);
+
+  // scale indices
+  int sa_idx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int m = m0 + wm * 64 + 16 * i + fr;
+    if (A_BLK == 1) {
+      sa_idx[i] = m < p.M ? m : p.M - 1;
+    } else {
+      int rb = (m0 + wm * 64) / 128;
+      sa_idx[i] = rb < p.sa_stride ? rb : p.sa_stride - 1;
+    }
+  }
+  int nb = (n0 + wn * 128) / 128;
+  nb = nb < p.sb_stride ? nb : p.sb_stride - 1;
+
+  v4f acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  float sa_cur[4], sa_nxt[4];
+  float sb_cur, sb_nxt;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sa_cur[i] = p.sa[sa_idx[i]];
+  sb_cur = sbbase[nb];
+
+  lda.issue(p.a, lds0, wave, 0);
+  ldb.issue(bbase, lds0 + A_BYTES, wave, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](const uint8_t* cur, uint8_t* nxt, int kb) {
+    // The last step re-stages the final K slice into the idle buffer so the
+    // body stays one basic block (the scheduling hints below need that).
+    const int kn = kb + 1 < p.nkb ? kb + 1 : kb;
+    lda.issue(p.a, nxt, wave, kn);
+    ldb.issue(bbase, nxt + A_BYTES, wave, kn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa_nxt[i] = p.sa[(int64_t)kn * p.sa_stride + sa_idx[i]];
+    sb_nxt = sbbase[(int64_t)kn * p.sb_stride + nb];
+    float s[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = sa_cur[i] * sb_cur;
+
+    v8i af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = read_frag(cur, wm * 64 + 16 * i, off0, off1);
+    v8i bf[2];
+    bf[0] = read_frag(cur + A_BYTES, wn * 128, off0, off1);
+    // 32 MFMAs in (j, i) order.  The 4 promotion FMAs of MFMA t are issued
+    // after MFMA t+1, so they overlap the matrix core instead of stalling on
+    // its result; the next B fragment is read right after the first MFMA of
+    // each group of four.  The fences pin this order against the scheduler,
+    // which otherwise hoists all MFMAs and parks 32 partials in registers.
+    v4f part[2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int j = t >> 2, i = t & 3;
+      part[t & 1] =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], zero, 0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 0 && j < 7) {
+        bf[(j + 1) & 1] = read_frag(cur + A_BYTES, wn * 128 + 16 * (j + 1), off0, off1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (t > 0) {
+        const int tp = t - 1, jp = tp >> 2, ip = tp & 3;
+        acc[ip][jp] += part[tp & 1] * s[ip];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    acc[3][7] += part[1] * s[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa_cur[i] = sa_nxt[i];
+    }
+    sb_cur = sb_nxt;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  for (int kb = 0; kb < p.nkb; kb += 2) {
+    step(lds0, lds1, kb);
+    if (kb + 1 < p.nkb) step(lds1, lds0, kb + 1);
+  }
+
+  // epilogue: BF16 round-to-nearest-even, 4 consecutive columns per lane
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 64 + 16 * i + fr;
+    if (m >= p.M) continue;
+    bool zero_row = false;
+    if (GROUPED) zero_row = p.m_indices[m] < 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
+      if (n < p.N) {
+        uint2 v;
+        if (zero_row) {
+          v = make_uint2(0, 0);
+        } else {
+          v.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+          v.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        }
+        *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = v;
+      }
+    }
+  }
+}
+
+template <int BM, int A_BLK, bool GROUPED>
+hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
+  TiledArgs p;
+  p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.m_indices = q.m_indices; p.num_groups = q.num_groups;
+  p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
+  p.nkb = (int)(q.K / BK);
+  p.sa_stride = (int)((q.M + q.a_block_rows - 1) / q.a_block_rows);
+  p.sb_stride = (int)((q.N + 127) / 128);
+  p.tiles_m = (int)((q.M + BM - 1) / BM);
+  p.tiles_n = (int)((q.N + BN - 1) / BN);
+  p.group_m = GROUPED ? 2 : 4;
+  const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+  hipLaunchKernelGGL((gemm_tiled_kernel<BM, A_BLK, GROUPED>), dim3(grid), dim3(BM * BN / 128),
+                     0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tiled(const GemmProblem& q, bool grouped, hipStream_t stream) {
+  if (grouped) {
+    return q.a_block_rows == 1 ? launch_one<128, 1, true>(q, stream)
+                               : launch_one<128, 128, true>(q, stream);
+  }
+  return q.a_block_rows == 1 ? launch_one<256, 1, false>(q, stream)
+                             : launch_one<256, 128, false>(q, stream);
+}
+
+}  // namespace dg

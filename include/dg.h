@@ -1,0 +1,126 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) FP8 block-scaled GEMM library
+ * (libdg.so).  C99-compatible; no HIP or PyTorch types appear here.
+ *
+ * The operations follow two public pages:
+ *   [Q] "DeepGEMM ... FP8 block-quantised GEMM" (lpnh.cn/news/2826317)
+ *   [D] "DeepGEMM: GPU high-efficiency BLAS kernel library" (pzsr.cn/news/21800)
+ *
+ * Conventions for every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or retains them.  They must stay valid until the
+ *     work queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Calls are asynchronous and stream-ordered.
+ *   - Arguments are validated on the host first.  On any error a non-zero
+ *     status is returned and NOTHING is enqueued.  DG_ERR_HIP means a launch
+ *     failed; faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - FP8 means E4M3 ("FN" encoding: bias 7, no infinities, S.1111.111 = NaN,
+ *     largest finite 448) [Q s2.2, s3.1].  BF16 outputs are raw 16-bit
+ *     patterns (uint16_t), rounded to nearest-even from FP32.
+ *   - Scale arrays are FP32, K-block-major: the scale of row-block rb and
+ *     K-block kb sits at scales[kb * n_row_blocks + rb] [Q s3.1: a separate
+ *     array indexed by block, accessed contiguously].
+ *   - Inputs must be finite.  Behaviour on NaN/Inf inputs is unspecified.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DG_ABI_VERSION 1
+
+enum {
+    DG_OK = 0,
+    DG_ERR_NULL = 1,        /* a required pointer is NULL                   */
+    DG_ERR_SHAPE = 2,       /* a size is negative, zero or not a multiple   */
+    DG_ERR_UNSUPPORTED = 3, /* block_rows / group count not supported       */
+    DG_ERR_ALIGN = 4,       /* a pointer is not suitably aligned            */
+    DG_ERR_WORKSPACE = 5,   /* workspace given but smaller than required    */
+    DG_ERR_HIP = 6          /* the HIP runtime reported an error            */
+};
+
+/* ABI version of the loaded library (compare with DG_ABI_VERSION). */
+int dg_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *dg_status_string(int status);
+
+/* Row alignment each expert's group must be padded to in the grouped,
+ * M-contiguous layout [D s3.3]: 128. */
+int dg_get_mk_alignment_for_contiguous_layout(void);
+
+/*
+ * Block quantiser [Q s4.2 steps 1-5, s3.1, s5.4; D s4.1 to_fp8].
+ *   x      : FP32 [rows][cols], row-major, 16-byte aligned.
+ *   q      : out, E4M3 codes [rows][cols], same layout, 16-byte aligned.
+ *   scales : out, FP32 [ceil(cols/128)][ceil(rows/block_rows)], 4-byte aligned.
+ *   block_rows : 128 (128x128 blocks, weights) or 1 (1x128, per-row
+ *            activation groups).  Edge blocks are clipped to the matrix.
+ * For each block: amax = max|x|; s = amax / 448 (binary32 division);
+ * s == 0 (all-zero block) gives codes +-0 with the element's sign; otherwise
+ * q = round-to-nearest-even-E4M3(binary32(x / s)), saturating at 448.
+ * Requirements: rows >= 1, cols >= 1, cols % 16 == 0.
+ */
+int dg_quantize_fp8_block(uint8_t *q, float *scales, const float *x,
+                          int64_t rows, int64_t cols, int block_rows, void *stream);
+
+/*
+ * Workspace bytes dg_fp8_gemm_nt can use for split-K on this shape (0 when
+ * the chosen plan needs none).  Passing a smaller, non-NULL workspace is an
+ * error; passing NULL/0 selects a plan that needs none.
+ */
+size_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * NT GEMM with fine-grained block scaling [Q s2.2, s3.2; D s3.1, s4.1]:
+ *   C[m][n] = bf16( sum_kb sa(m,kb) * sb(n,kb) * sum_{k in kb} A[m][k] * B[n][k] )
+ * with FP32 accumulation and promotion once per 128-wide K block.
+ *   c  : out, BF16 [M][N] row-major, 16-byte aligned.
+ *   a  : E4M3 [M][K] row-major (K contiguous), 16-byte aligned.
+ *   b  : E4M3 [N][K] row-major (K contiguous), 16-byte aligned.
+ *   sa : FP32 [K/128][ceil(M/a_block_rows)], a_block_rows in {1, 128}.
+ *   sb : FP32 [K/128][ceil(N/128)] (128x128 blocks).
+ *   workspace / workspace_bytes: optional device scratch for split-K on
+ *        small-M shapes (see dg_fp8_gemm_nt_workspace_bytes); may be NULL/0.
+ *        Its contents need not be initialised and are clobbered.
+ * Requirements: M >= 1; N >= 8, N % 8 == 0; K >= 128, K % 128 == 0.
+ * The result is deterministic: a given plan sums in a fixed order.
+ */
+int dg_fp8_gemm_nt(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                   const float *sa, const float *sb, int a_block_rows,
+                   int64_t M, int64_t N, int64_t K,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Grouped GEMM, experts contiguous along M [D s2.3, s3.2, s3.3]:
+ *   a         : E4M3 [M][K]; the rows of each expert are contiguous, experts
+ *               in ascending id, each group padded to a multiple of 128 rows.
+ *   b         : E4M3 [num_groups][N][K]; sb: FP32 [num_groups][K/128][ceil(N/128)].
+ *   sa        : FP32 [K/128][ceil(M/a_block_rows)], a_block_rows in {1, 128}.
+ *   m_indices : int32 [M]: expert id of each row, or -1 for a padding row.
+ *               Within one 128-row block every row holds the same id or -1,
+ *               and the block's first row holds the id (or the whole block
+ *               is padding).
+ *   c         : out, BF16 [M][N]; padding rows are written as zeros.
+ * Row m computes C[m] = A[m] . B[g]^T with g = m_indices[m], scales as in
+ * dg_fp8_gemm_nt using sb + g * (K/128) * ceil(N/128).
+ * Requirements: M >= 128, M % 128 == 0; N >= 8, N % 8 == 0; K % 128 == 0;
+ * 1 <= num_groups.  Ids outside [-1, num_groups) are a contract violation
+ * (such rows are written as zeros).
+ */
+int dg_fp8_grouped_gemm_contig(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                               const float *sa, const float *sb, int a_block_rows,
+                               const int32_t *m_indices, int num_groups,
+                               int64_t M, int64_t N, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DG_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every entry point declared in
+include/dg.h, and rejects bad arguments on the host before any HIP call
+(these calls enqueue nothing and need no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "dg.h")
+
+
+@pytest.fixture(scope="module")
+def dg():
+    import fp8_block_scaled_dg_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for need in ("dg_quantize_fp8_block", "dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contig",
+                 "dg_abi_version", "dg_status_string", "dg_fp8_gemm_nt_workspace_bytes",
+                 "dg_get_mk_alignment_for_contiguous_layout"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(dg):
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(dg):
+    assert dg.lib.dg_abi_version() == 1
+    for st in range(0, 7):
+        assert dg.status_string(st) and dg.status_string(st) != "unknown status"
+    assert dg.status_string(99) == "unknown status"
+    assert dg.get_mk_alignment_for_contiguous_layout() == 128
+
+
+P = ctypes.c_void_p(0x10000)   # dummy, 16-byte aligned, never dereferenced
+P1 = ctypes.c_void_p(0x10001)  # misaligned
+
+
+def q(lib, qp=P, sp=P, xp=P, rows=128, cols=128, br=128):
+    return lib.dg_quantize_fp8_block(qp, sp, xp, rows, cols, br, None)
+
+
+def test_quantize_validation(dg):
+    lib = dg.lib
+    assert q(lib, qp=None) == 1
+    assert q(lib, sp=None) == 1
+    assert q(lib, xp=None) == 1
+    assert q(lib, br=64) == 3
+    assert q(lib, rows=0) == 2
+    assert q(lib, cols=0) == 2
+    assert q(lib, cols=24) == 2          # cols % 16
+    assert q(lib, rows=-5) == 2
+    assert q(lib, rows=128 * 70000) == 2  # grid limit
+    assert q(lib, xp=P1) == 4
+    assert q(lib, qp=P1) == 4
+
+
+def g(lib, c=P, a=P, b=P, sa=P, sb=P, br=128, M=256, N=256, K=256, ws=None, wsb=0):
+    return lib.dg_fp8_gemm_nt(c, a, b, sa, sb, br, M, N, K, ws, wsb, None)
+
+
+def test_gemm_validation(dg):
+    lib = dg.lib
+    for kw in ("c", "a", "b", "sa", "sb"):
+        assert g(lib, **{kw: None}) == 1
+    assert g(lib, br=2) == 3
+    assert g(lib, M=0) == 2
+    assert g(lib, N=4) == 2
+    assert g(lib, N=260) == 2            # N % 8
+    assert g(lib, K=64) == 2
+    assert g(lib, K=200) == 2            # K % 128
+    assert g(lib, M=70000, K=65536 + 128) == 2   # 32-bit offsets
+    assert g(lib, a=P1) == 4
+    assert g(lib, sa=ctypes.c_void_p(0x10002)) == 4
+
+
+def gg(lib, mi=P, G=2, M=256, N=256, K=256, br=1):
+    return lib.dg_fp8_grouped_gemm_contig(P, P, P, P, P, br, mi, G, M, N, K, None)
+
+
+def test_grouped_validation(dg):
+    lib = dg.lib
+    assert gg(lib, mi=None) == 1
+    assert gg(lib, G=0) == 3
+    assert gg(lib, M=200) == 2            # M % 128
+    assert gg(lib, K=100) == 2
+    assert gg(lib, mi=ctypes.c_void_p(0x10002)) == 4
+
+
+def test_workspace_query_is_host_only(dg):
+    assert dg.dg_fp8_gemm_nt_workspace_bytes(1, 4096, 4096) >= 0
+    assert dg.dg_fp8_gemm_nt_workspace_bytes(0, 4096, 4096) == 0

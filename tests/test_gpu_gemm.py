@@ -1,0 +1,163 @@
+"""GPU NT GEMM parity against the FP64 oracle (lpnh.cn FP8 block-quantised GEMM
+page s2.2, s3.2; NT layout per the pzsr.cn DeepGEMM page s3.1, s4.1).
+
+The oracle quantises the seeded FP32 inputs; its codes and scales are fed to
+the GPU GEMM, so GEMM parity does not depend on the GPU quantiser.  Small
+shapes are compared element by element in full; full-size shapes on sampled
+elements (random points plus whole rows and columns and the corners)."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dg():
+    need_gpu()
+    import fp8_block_scaled_dg_amd as m
+    return m
+
+
+def run_gemm(dg, qa, sa, qb, sb, br, workspace=None):
+    M, K = qa.shape
+    N = qb.shape[0]
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm_nt(c, dev(qa), dev(qb), dev(sa), dev(sb), br, workspace=workspace)
+    torch.cuda.synchronize()
+    return c
+
+
+def operands(orc, M, N, K, br, seed=0, sig_a=1.0, sig_b=0.02):
+    a = datagen.normal((M, K), sig_a, seed=seed, stream=0)
+    b = datagen.normal((N, K), sig_b, seed=seed, stream=1)
+    qa, sa = orc.quantize(a, br)
+    qb, sb = orc.quantize(b, 128)
+    return qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("br", [128, 1])
+@pytest.mark.parametrize("M,N,K", [
+    (128, 256, 512),      # the small single-GEMM case
+    (256, 256, 128), (512, 768, 384), (300, 520, 1024), (200, 264, 256),
+    (1, 256, 256), (16, 512, 512), (64, 4096, 512), (33, 1000, 640), (257, 136, 128)])
+def test_gemm_small_full_compare(dg, orc, M, N, K, br):
+    qa, sa, qb, sb = operands(orc, M, N, K, br, seed=M + N + K)
+    ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=br)
+    c = bf16_to_f64(run_gemm(dg, qa, sa, qb, sb, br))
+    assert_close(c, ref, what="%dx%dx%d/%d" % (M, N, K, br))
+
+
+def test_gemm_exactness_probe_is_bit_exact(dg, orc):
+    """Unit scales and codes for 0, +-1, +-2 (lpnh.cn page s6): every output is
+    an integer of magnitude <= 512, exactly representable in BF16."""
+    g = np.random.default_rng(3)
+    codes = np.array([0x00, 0x38, 0xB8, 0x40, 0xC0], dtype=np.uint8)
+    vals = np.array([0, 1, -1, 2, -2], dtype=np.int64)
+    M, N, K = 256, 512, 128
+    ia = g.integers(0, 5, size=(M, K))
+    ib = g.integers(0, 5, size=(N, K))
+    ones = np.ones((1, 2), np.float32)
+    want = (vals[ia] @ vals[ib].T).astype(np.float64)
+    for br, sa in ((128, np.ones((1, 2), np.float32)), (1, np.ones((1, M), np.float32))):
+        c = bf16_to_f64(run_gemm(dg, codes[ia], sa, codes[ib], np.ones((1, 4), np.float32), br))
+        assert np.array_equal(c, want)
+    del ones
+
+
+def test_gemm_one_hot_layout_probes(dg, orc):
+    """A single 1.0 in A at (m, k) must reproduce sa*sb*B[:, k] in row m and
+    zeros elsewhere: pins the MFMA operand/accumulator layout and the edges."""
+    g = np.random.default_rng(4)
+    M, N, K = 300, 520, 384
+    b = datagen.normal((N, K), 0.02, seed=9)
+    qb, sb = orc.quantize(b, 128)
+    sa = np.full((K // 128, M), 0.5, np.float32)
+    for (m, k) in [(0, 0), (299, 383), (17, 130), (255, 127), (256, 256)]:
+        qa = np.zeros((M, K), np.uint8)
+        qa[m, k] = 0x38
+        ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=1)
+        c = bf16_to_f64(run_gemm(dg, qa, sa, qb, sb, 1))
+        assert np.count_nonzero(c[np.arange(M) != m]) == 0
+        assert_close(c, ref, what="one-hot %d,%d" % (m, k))
+    del g
+
+
+def test_gemm_power_of_two_scale_exchange_identical_bits(dg, orc):
+    qa, sa, qb, sb = operands(orc, 256, 512, 384, 1, seed=5)
+    c1 = run_gemm(dg, qa, sa, qb, sb, 1)
+    c2 = run_gemm(dg, qa, sa * np.float32(8.0), qb, sb * np.float32(0.125), 1)
+    assert torch.equal(c1, c2)
+
+
+def test_gemm_deterministic(dg, orc):
+    qa, sa, qb, sb = operands(orc, 512, 1024, 1024, 128, seed=6)
+    c1 = run_gemm(dg, qa, sa, qb, sb, 128)
+    c2 = run_gemm(dg, qa, sa, qb, sb, 128)
+    assert torch.equal(c1, c2)
+
+
+def sample_points(M, N, n_rand=1500, seed=0):
+    g = np.random.default_rng(seed)
+    pm = [g.integers(0, M, n_rand)]
+    pn = [g.integers(0, N, n_rand)]
+    for m in (0, M - 1, M // 2 + 3):              # whole rows
+        pm.append(np.full(N, m))
+        pn.append(np.arange(N))
+    for n in (0, N - 1, N // 3 + 1):              # whole columns (capped)
+        rows = np.arange(0, M, max(1, M // 512))
+        pm.append(rows)
+        pn.append(np.full(rows.shape, n))
+    return np.concatenate(pm), np.concatenate(pn)
+
+
+@pytest.mark.parametrize("M,N,K,br", [(4096, 7168, 2048, 128), (4096, 4096, 7168, 128),
+                                      (8192, 8192, 8192, 128), (8192, 8192, 8192, 1)])
+def test_gemm_full_size_sampled(dg, orc, M, N, K, br):
+    qa, sa, qb, sb = operands(orc, M, N, K, br, seed=0)
+    c = run_gemm(dg, qa, sa, qb, sb, br)
+    pm, pn = sample_points(M, N, seed=M + N)
+    ref = orc.gemm_nt_points(qa, sa, qb, sb, pm, pn, a_block_rows=br)
+    got = c[torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()]
+    got = got.float().cpu().numpy().astype(np.float64)
+    # rms of the full output estimated from the random points
+    rms = float(np.sqrt(np.mean(ref[:1500] ** 2)))
+    assert_close(got, ref, rms=rms, what="%dx%dx%d/%d" % (M, N, K, br))
+    assert torch.isfinite(c.float()).all()
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("N,K", [(24576, 1536), (7168, 16384), (4096, 4096)])
+def test_gemm_decode_shapes_sampled(dg, orc, M, N, K):
+    qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=M)
+    ws_bytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    c = run_gemm(dg, qa, sa, qb, sb, 1, workspace=ws)
+    c_nows = run_gemm(dg, qa, sa, qb, sb, 1, workspace=None)
+    pm, pn = sample_points(M, N, seed=N)
+    ref = orc.gemm_nt_points(qa, sa, qb, sb, pm, pn, a_block_rows=1)
+    rms = float(np.sqrt(np.mean(ref[:1500] ** 2)))
+    for cc in (c, c_nows):
+        got = cc[torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()]
+        assert_close(got.float().cpu().numpy().astype(np.float64), ref, rms=rms,
+                     what="decode %dx%dx%d" % (M, N, K))
+
+
+def test_end_to_end_quantise_then_gemm(dg, orc):
+    """GPU quantiser + GPU GEMM on the small single-GEMM case against the
+    oracle quantiser + oracle GEMM (same FP32 inputs)."""
+    M, N, K = 128, 256, 512
+    a = datagen.normal((M, K), 1.0, seed=0, stream=0)
+    b = datagen.normal((N, K), 1.0, seed=0, stream=1)
+    qa, sa = dg.to_fp8(dev(a), 128)
+    qb, sb = dg.to_fp8(dev(b), 128)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.fp8_gemm_nt(c, qa, qb, sa, sb, 128)
+    torch.cuda.synchronize()
+    oqa, osa = orc.quantize(a, 128)
+    oqb, osb = orc.quantize(b, 128)
+    ref = orc.gemm_nt(oqa, osa, oqb, osb, a_block_rows=128)
+    assert_close(bf16_to_f64(c), ref, what="end-to-end")

@@ -1,0 +1,103 @@
+"""GPU quantiser parity: codes and scales must equal the oracle bit for bit
+(the quantisation recipe of the lpnh.cn FP8 block-quantised GEMM page, s3.1,
+s4.2, s5.4, has a unique result).  Calls go through the C ABI."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from gpu_util import dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def dg():
+    need_gpu()
+    import fp8_block_scaled_dg_amd as m
+    return m
+
+
+def gpu_quant(dg, x, br):
+    q, s = dg.to_fp8(dev(x), br)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def check(dg, orc, x, br, what):
+    q, s = gpu_quant(dg, x, br)
+    oq, os_ = orc.quantize(x, br)
+    assert np.array_equal(s.view(np.uint32), os_.view(np.uint32)), what + ": scales differ"
+    bad = np.argwhere(q != oq)
+    assert bad.size == 0, "%s: %d codes differ, first %s gpu %s oracle %s x %r" % (
+        what, len(bad), bad[:3].tolist(), q[tuple(bad[0])], oq[tuple(bad[0])], x[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("br", [128, 1])
+@pytest.mark.parametrize("rows,cols", [(128, 512), (256, 512), (1, 128), (3, 16), (200, 384),
+                                       (129, 1024), (300, 144), (64, 400)])
+def test_quantize_small_and_ragged(dg, orc, rows, cols, br):
+    x = datagen.normal((rows, cols), 1.0, seed=rows * 7 + cols, stream=br)
+    check(dg, orc, x, br, "%dx%d/%d" % (rows, cols, br))
+
+
+@pytest.mark.parametrize("br", [128, 1])
+def test_quantize_special_blocks(dg, orc, br):
+    x = datagen.normal((256, 640), 0.02, seed=3)
+    x[:128, :128] = 0.0                      # all-zero block
+    x[5, 7] = -0.0
+    x[:, 128:256] *= np.float32(1e-38)       # amax/448 is subnormal: IEEE division path
+    x[130:, 256:384] *= np.float32(1e-30)    # tiny but normal scale
+    x[:, 384:512] = np.float32(2.0) ** np.arange(-20, 108, dtype=np.float32)[None, :]
+    x[3, 512:] = -np.abs(x[3, 512:])
+    check(dg, orc, x, br, "special/%d" % br)
+
+
+def test_two_step_rounding_vectors_on_gpu(dg, orc):
+    """Blocks built so that s = binary32(amax/448) equals the vector's s and
+    the block holds x: the quotient x/s rounds to an E4M3 midpoint in binary32."""
+    with open(os.path.join(GOLDEN, "two_step_rounding.json")) as f:
+        vecs = json.load(f)["vectors"]
+    x = np.zeros((len(vecs), 128), dtype=np.float32)
+    expect = []
+    for r, v in enumerate(vecs):
+        xv = np.array([int(v["x_hex"], 16)], np.uint32).view(np.float32)[0]
+        sv = np.array([int(v["s_hex"], 16)], np.uint32).view(np.float32)[0]
+        amax = np.float32(sv * np.float32(448.0))
+        for _ in range(64):                  # nudge amax until amax/448 gives s exactly
+            got = amax / np.float32(448.0)
+            if got == sv:
+                break
+            amax = np.nextafter(amax, np.float32(np.inf) if got < sv else np.float32(0))
+        assert amax / np.float32(448.0) == sv
+        x[r, 0] = amax
+        x[r, 1] = xv
+        expect.append(int(v["code"], 16))
+    q, s = gpu_quant(dg, x, 1)
+    assert q[:, 1].tolist() == expect
+    check(dg, orc, x, 1, "r3")
+
+
+@pytest.mark.parametrize("what,rows,cols,br", [
+    ("C2a A", 4096, 2048, 128), ("C2c B", 8192, 8192, 128), ("C3 A M=64", 64, 16384, 1),
+    ("C4 down A", 2816, 11008, 1)])
+def test_quantize_full_size(dg, orc, what, rows, cols, br):
+    x = datagen.normal((rows, cols), 1.0 if br == 1 else 0.02, seed=0, stream=1)
+    check(dg, orc, x, br, what)
+
+
+def test_quantize_outlier_activations(dg, orc):
+    x, hot = datagen.student_t_outliers(1024, 8192, seed=0, stream=5)
+    check(dg, orc, x, 1, "C5 A rows")
+    check(dg, orc, x, 128, "C5 A rows global-ish")
+
+
+def test_quantize_deterministic(dg):
+    x = dev(datagen.normal((1024, 2048), 1.0, seed=4))
+    q1, s1 = dg.to_fp8(x, 128)
+    q2, s2 = dg.to_fp8(x, 128)
+    assert torch.equal(q1, q2) and torch.equal(s1, s2)
