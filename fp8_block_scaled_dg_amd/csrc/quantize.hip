@@ -28,15 +28,17 @@ __device__ __forceinline__ float quotient_rn(float x, float s, float r) {
   return __builtin_fmaf(e, r, q);
 }
 
+// The quotient is formed on |x| (s > 0, so |x/s| = |x|/s) and the sign bit is
+// copied from x: the FMA correction would turn a -0 quotient into +0.
+__device__ __forceinline__ uint32_t encode1(float x, float s, float r, bool slow) {
+  const float ax = fabsf(x);
+  const float v = slow ? ax / s : quotient_rn(ax, s, r);
+  return e4m3_rne_mag(v) | ((__float_as_uint(x) >> 24) & 0x80u);
+}
+
 __device__ __forceinline__ uint32_t encode4(float4 v, float s, float r, bool slow) {
-  float a0, a1, a2, a3;
-  if (slow) {
-    a0 = v.x / s; a1 = v.y / s; a2 = v.z / s; a3 = v.w / s;
-  } else {
-    a0 = quotient_rn(v.x, s, r); a1 = quotient_rn(v.y, s, r);
-    a2 = quotient_rn(v.z, s, r); a3 = quotient_rn(v.w, s, r);
-  }
-  return e4m3_rne(a0) | (e4m3_rne(a1) << 8) | (e4m3_rne(a2) << 16) | (e4m3_rne(a3) << 24);
+  return encode1(v.x, s, r, slow) | (encode1(v.y, s, r, slow) << 8) |
+         (encode1(v.z, s, r, slow) << 16) | (encode1(v.w, s, r, slow) << 24);
 }
 
 __device__ __forceinline__ uint32_t zero_codes4(float4 v) {

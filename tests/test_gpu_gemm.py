@@ -104,10 +104,10 @@ def sample_points(M, N, n_rand=1500, seed=0):
     g = np.random.default_rng(seed)
     pm = [g.integers(0, M, n_rand)]
     pn = [g.integers(0, N, n_rand)]
-    for m in (0, M - 1, M // 2 + 3):              # whole rows
+    for m in sorted({0, M - 1, min(M - 1, M // 2 + 3)}):   # whole rows
         pm.append(np.full(N, m))
         pn.append(np.arange(N))
-    for n in (0, N - 1, N // 3 + 1):              # whole columns (capped)
+    for n in sorted({0, N - 1, min(N - 1, N // 3 + 1)}):   # whole columns (capped)
         rows = np.arange(0, M, max(1, M // 512))
         pm.append(rows)
         pn.append(np.full(rows.shape, n))

@@ -19,8 +19,8 @@ def dg():
     return m
 
 
-def build(orc, tokens, G, N, K, br, seed, hidden_from_tokens=True, drop_expert=None):
-    r = datagen.moe_routing(tokens, G, 2, align=128, seed=seed)
+def build(orc, tokens, G, N, K, br, seed, drop_expert=None):
+    r = datagen.moe_routing(tokens, G, min(2, G), align=128, seed=seed)
     mi = r["m_indices"].copy()
     if drop_expert is not None:                  # an expert with no rows at all
         starts = np.concatenate([[0], np.cumsum(r["padded"])])

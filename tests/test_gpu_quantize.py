@@ -54,6 +54,7 @@ def test_quantize_special_blocks(dg, orc, br):
     x[130:, 256:384] *= np.float32(1e-30)    # tiny but normal scale
     x[:, 384:512] = np.float32(2.0) ** np.arange(-20, 108, dtype=np.float32)[None, :]
     x[3, 512:] = -np.abs(x[3, 512:])
+    x[10, 300] = x[200, 20] = x[7, 600] = x[255, 639] = -0.0   # -0 inside non-zero blocks
     check(dg, orc, x, br, "special/%d" % br)
 
 
