@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 OBJDIR = os.path.join(LIBDIR, "obj")
 LIB = os.path.join(LIBDIR, "libdg.so")
-SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "gemm_stream.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -3,6 +3,7 @@
 // a rejected call enqueues nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/dg.h"
 #include "dg_internal.hpp"
@@ -87,7 +88,10 @@ int dg_fp8_gemm_nt(uint16_t* c, const uint8_t* a, const uint8_t* b, const float*
   }
   dg::GemmProblem p{c, a, b, sa, sb, nullptr, 1, a_block_rows, M, N, K};
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (skinny) return from_hip(dg::launch_gemm_skinny(p, workspace, workspace_bytes, s));
+  if (skinny) {
+    if (dg::stream_preferred(M, N, K)) return from_hip(dg::launch_gemm_stream(p, s));
+    return from_hip(dg::launch_gemm_skinny(p, workspace, workspace_bytes, s));
+  }
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles > INT32_MAX) return DG_ERR_SHAPE;
   return from_hip(dg::launch_gemm_tiled(p, false, s));

@@ -32,4 +32,9 @@ bool skinny_applies(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const GemmProblem& p, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+// Streaming small-M kernel (no workspace), and whether it is the better of
+// the two small-M kernels for a shape.
+hipError_t launch_gemm_stream(const GemmProblem& p, hipStream_t stream);
+bool stream_preferred(int64_t M, int64_t N, int64_t K);
+
 }  // namespace dg

@@ -1,16 +1,351 @@
-// Small-M (decode) FP8 block-scaled NT GEMM for gfx950.  Not yet specialised:
-// every shape currently runs on the tiled kernel.
+// Small-M (decode) FP8 block-scaled NT GEMM for gfx950.
+//
+// Same operation as the tiled kernel (FP8 block-quantised GEMM page on
+// lpnh.cn, s2.2 and s3.2; NT layout per the DeepGEMM page on pzsr.cn, s3.1),
+// for M <= 64 where the work is bound by streaming B (N x K bytes) from HBM:
+// the lpnh.cn page (s3.4, s4.3, s5.5) notes that the kernel picks its tile and
+// pipeline depth from the shape, and that on small problems loading the
+// scales/operands rather than arithmetic dominates.
+//
+// gfx950 mapping
+//  * A workgroup (4 waves) owns 128 rows of B (one 128-row scale block) and a
+//    contiguous range of K blocks.  B streams through a 3-stage LDS ring fed by
+//    global_load_lds_dwordx4 (16 KB of B per stage, 8 consecutive lanes per
+//    128-byte row, chunk permutation as in the tiled kernel); a workgroup
+//    needs <= 75 KB of LDS, so two run per CU with 4 stages (64 KB) of B in
+//    flight between them.  A (M padded to 16/32/64 rows, rows past M clamped)
+//    and its 1x128 (or 128x128) scales, and the B block scale, ride in the
+//    same stages.  The ring slots are distinct __shared__ arrays and the loop
+//    is unrolled by the ring depth, so the compiler's LDS-DMA dependency
+//    tracking can see that the slot being filled is not the slot being read
+//    (with one array it waits for every outstanding load before each read).
+//  * Each wave computes 32 rows of B x MP columns of A with
+//    v_mfma_f32_16x16x128_f8f6f4 (B rows drive the instruction's first
+//    operand), promoting each 128-K partial with sa*sb in FP32.
+//  * Split-K when N/128 workgroups cannot fill the GPU: split s writes its
+//    FP32 partial tile to the caller's workspace, then the last split to
+//    arrive (device-scope counter) sums the S partials in split order and
+//    writes BF16, so the result does not depend on arrival order.  Counters
+//    live in a static device array that starts at zero and is reset by the
+//    reducing workgroup, so every call leaves it zeroed.  Two calls that
+//    overlap on one GPU (different streams) must not both use split-K.
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
+#include <stdlib.h>
+
 namespace dg {
+namespace {
 
-bool skinny_applies(int64_t, int64_t, int64_t) { return false; }
+constexpr int BN = 128;
+constexpr int BK = 128;
+constexpr int NS = 3;              // LDS ring depth (<= 75 KB: two workgroups per CU)
+constexpr int kMaxCounters = 8192; // N up to 1M with BN = 128
+constexpr int kMaxSplits = 16;
 
-size_t skinny_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+__device__ int g_splitk_counters[kMaxCounters];
 
-hipError_t launch_gemm_skinny(const GemmProblem&, void*, size_t, hipStream_t) {
-  return hipErrorNotSupported;
+struct SkinnyArgs {
+  uint16_t* c;
+  const uint8_t* a;
+  const uint8_t* b;
+  const float* sa;
+  const float* sb;
+  float* partials;  // [S][M][N] when S > 1
+  int a_block_rows;
+  int M, N, K;
+  int nkb;
+  int sa_stride;  // ceil(M / a_block_rows)
+  int sb_stride;  // ceil(N / 128)
+  int S;          // K splits
+};
+
+__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 1); }
+
+__device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int off0, int off1) {
+  const v4i lo = *reinterpret_cast<const v4i*>(lds + row_base * 128 + off0);
+  const v4i hi = *reinterpret_cast<const v4i*>(lds + row_base * 128 + off1);
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+template <int MP>
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
+  constexpr int MPE = MP < 32 ? 32 : MP;          // A rows staged (>= 4 DMA instructions)
+  constexpr int B_BYTES = BN * BK;                // 16 KB
+  constexpr int A_BYTES = MPE * BK;
+  constexpr int SA_BYTES = 4 * 256;               // one 64-float copy per wave
+  constexpr int SB_BYTES = 4 * 256;               // B block scale (64 copies) per wave
+  constexpr int STAGE = B_BYTES + A_BYTES + SA_BYTES + SB_BYTES;
+  constexpr int B_IT = B_BYTES / 1024 / 4;        // DMA instructions per wave per stage
+  constexpr int A_IT = A_BYTES / 1024 / 4;
+  constexpr int PER_STAGE = B_IT + A_IT + 2;      // + the A scale row + the B scale
+  constexpr int NI = MP / 16;                     // A fragments
+  static_assert(NS == 3, "the ring below is written out for three slots");
+  __shared__ __attribute__((aligned(1024))) uint8_t l0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t l1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t l2[STAGE];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nt = blockIdx.x / p.S;
+  const int split = blockIdx.x - nt * p.S;
+  const int n0 = nt * BN;
+  const int kb0 = (int)((int64_t)split * p.nkb / p.S);
+  const int kb1 = (int)((int64_t)(split + 1) * p.nkb / p.S);
+  const int nk = kb1 - kb0;  // >= 1 (S <= nkb)
+
+  // DMA source offsets (bytes, at kb = 0).  Instruction j of wave w fills the
+  // 1 KB at LDS offset (j*4 + w)*1024 of the B (or A) region: rows 8*(j*4+w)
+  // .. +7, lane L -> row +L/8, physical chunk L%8.
+  uint32_t boff[B_IT], aoff[A_IT];
+#pragma unroll
+  for (int j = 0; j < B_IT; ++j) {
+    const int r = (j * 4 + wave) * 8 + (lane >> 3);
+    int gr = n0 + r;
+    gr = gr < p.N ? gr : p.N - 1;
+    boff[j] = (uint32_t)gr * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ lds_swz(r)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < A_IT; ++j) {
+    const int r = (j * 4 + wave) * 8 + (lane >> 3);
+    const int gr = r < p.M ? r : p.M - 1;
+    aoff[j] = (uint32_t)gr * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ lds_swz(r)) * 16);
+  }
+  const int sa_row = p.a_block_rows == 1 ? (lane < p.M ? lane : p.M - 1) : 0;
+  const int nb = n0 / 128;  // the 128 rows of this workgroup form one B scale block
+
+  auto issue_stage = [&](int it, uint8_t* st) {
+    const int kb = kb0 + (it < nk ? it : nk - 1);  // past the range: re-stage the last block
+#pragma unroll
+    for (int j = 0; j < B_IT; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(p.b + boff[j] + (uint32_t)kb * BK),
+                                       (__attribute__((address_space(3))) void*)(st + (j * 4 + wave) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < A_IT; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(p.a + aoff[j] + (uint32_t)kb * BK),
+                                       (__attribute__((address_space(3))) void*)(st + B_BYTES + (j * 4 + wave) * 1024),
+                                       16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.sa + (int64_t)kb * p.sa_stride + sa_row),
+                                     (__attribute__((address_space(3))) void*)(st + B_BYTES + A_BYTES + wave * 256),
+                                     4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.sb + (int64_t)kb * p.sb_stride + nb),
+                                     (__attribute__((address_space(3))) void*)(st + B_BYTES + A_BYTES + SA_BYTES + wave * 256),
+                                     4, 0, 0);
+  };
+
+  const int fr = lane & 15;
+  const int off0 = fr * 128 + (((2 * (lane >> 4)) ^ lds_swz(fr)) * 16);
+  const int off1 = fr * 128 + (((2 * (lane >> 4) + 1) ^ lds_swz(fr)) * 16);
+
+  v4f acc[2][NI];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) acc[f][i] = v4f{0.f, 0.f, 0.f, 0.f};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  issue_stage(0, l0);
+  issue_stage(1, l1);
+
+  // one K block: stage `it` sits in `cur`; stage it+NS-1 goes into `nxt`
+  // (the slot of stage it-1, free once every wave has passed this barrier)
+  auto body = [&](int it, const uint8_t* cur, uint8_t* nxt) {
+    // this wave's loads for stage `it` have landed once at most the loads of
+    // the NS-2 younger stages remain outstanding (loads retire in order)
+    __builtin_amdgcn_s_waitcnt((((NS - 2) * PER_STAGE) & 15) | ((((NS - 2) * PER_STAGE) >> 4) << 14) |
+                               (0x7 << 4) | (0xF << 8));
+    // A bare barrier: __syncthreads() adds a workgroup release fence, which
+    // waits for every outstanding DMA write to LDS (all NS-1 stages in
+    // flight).  Every wave has waited for its own loads of stage `it` above,
+    // and has consumed its reads of stage it-1 (their results fed the MFMAs),
+    // so the barrier alone makes stage `it` complete and slot it-1 free.
+    asm volatile("s_barrier" ::: "memory");
+    issue_stage(it + NS - 1, nxt);
+
+    // Steps past the K range (the unrolled ring always runs whole rounds of
+    // three) re-read the last staged block with a zero scale: they add exactly
+    // 0, and they keep the loop free of branches, without which the
+    // compiler's LDS-DMA tracking falls back to waiting for every load.
+    const float sbv =
+        it < nk ? reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64] : 0.0f;
+    float s[NI];
+    const float* sa_l = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) s[i] = sa_l[16 * i + fr] * sbv;  // (all 64 slots equal for 128-row A blocks)
+    v8i af[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) af[i] = read_frag(cur + B_BYTES, 16 * i, off0, off1);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const v8i bf = read_frag(cur, wave * 32 + 16 * f, off0, off1);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const v4f part =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 0, 0, 0);
+        acc[f][i] += part * s[i];
+      }
+    }
+  };
+
+  for (int it = 0; it < nk; it += NS) {
+    body(it, l0, l2);
+    body(it + 1, l1, l0);
+    body(it + 2, l2, l1);
+  }
+  // drain the re-staged loads past the range before the workgroup exits
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+
+  // lane owns C[m = 16i + l%16][n = n0 + 32*wave + 16f + 4*(l/16) + r]
+  if (p.S == 1) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int m = 16 * i + fr;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int n = n0 + wave * 32 + 16 * f + 4 * (lane >> 4);
+        if (n < p.N) {
+          uint2 v;
+          v.x = bf16_rne(acc[f][i][0]) | (bf16_rne(acc[f][i][1]) << 16);
+          v.y = bf16_rne(acc[f][i][2]) | (bf16_rne(acc[f][i][3]) << 16);
+          *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = v;
+        }
+      }
+    }
+    return;
+  }
+
+  // split-K.  The 8 XCDs have separate L2s, so the partials are published
+  // with device-scope (relaxed atomic) stores, which are written through to
+  // the device-coherent level, and read back with device-scope loads; a full
+  // __threadfence() would instead write back each XCD's whole L2.
+  float* mine = p.partials + (int64_t)split * p.M * p.N;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int m = 16 * i + fr;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int n = n0 + wave * 32 + 16 * f + 4 * (lane >> 4);
+      if (n < p.N) {
+        float* d = mine + (int64_t)m * p.N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __hip_atomic_store(d + r, acc[f][i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // every store of this wave has completed (is device-visible) ...
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  __syncthreads();  // ... and so have those of every wave of the workgroup
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(&g_splitk_counters[nt], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == p.S - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // the last split sums the S partials in split order (deterministic) -> BF16
+  const int ncols = min(BN, p.N - n0);
+  for (int idx = threadIdx.x; idx < p.M * (BN / 4); idx += 256) {
+    const int m = idx / (BN / 4);
+    const int cc = (idx - m * (BN / 4)) * 4;
+    if (cc >= ncols) continue;
+    const int64_t o = (int64_t)m * p.N + n0 + cc;
+    // load every split's partial first (independent device-scope loads in
+    // flight together), then add them in split order
+    float4 part[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      if (sp < p.S) {
+        const float* src = p.partials + (int64_t)sp * p.M * p.N + o;
+        part[sp].x = __hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        part[sp].y = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        part[sp].z = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        part[sp].w = __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    float t[4] = {part[0].x, part[0].y, part[0].z, part[0].w};
+#pragma unroll
+    for (int sp = 1; sp < kMaxSplits; ++sp) {
+      if (sp < p.S) {
+        t[0] += part[sp].x; t[1] += part[sp].y; t[2] += part[sp].z; t[3] += part[sp].w;
+      }
+    }
+    uint2 v;
+    v.x = bf16_rne(t[0]) | (bf16_rne(t[1]) << 16);
+    v.y = bf16_rne(t[2]) | (bf16_rne(t[3]) << 16);
+    *reinterpret_cast<uint2*>(p.c + o) = v;
+  }
+  if (threadIdx.x == 0)  // leave the counter zeroed for the next call
+    __hip_atomic_store(&g_splitk_counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Optional override for tuning sweeps: DG_SKINNY_SPLITS=<S> (read once).
+int forced_splits() {
+  static const int v = [] {
+    const char* e = getenv("DG_SKINNY_SPLITS");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+int choose_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = (N + BN - 1) / BN;
+  const int64_t nkb = K / BK;
+  if (forced_splits() > 0) {
+    int64_t f = forced_splits();
+    f = f > nkb ? nkb : f;
+    return (int)(f > kMaxSplits ? kMaxSplits : f);
+  }
+  // ~one workgroup per CU; more splits only add partial traffic, which grows
+  // with M (measured best: 1 split at N = 24576, 4 at N = 4096 and 7168)
+  int64_t S = 256 / tiles;
+  S = S < 1 ? 1 : S;
+  S = S > 4 ? 4 : S;
+  S = S > nkb / 3 ? nkb / 3 : S;                // keep >= 3 K blocks (one ring round) per split
+  S = S < 1 ? 1 : S;
+  (void)M;
+  return (int)S;
+}
+
+}  // namespace
+
+bool skinny_applies(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 64 && (N + BN - 1) / BN <= kMaxCounters && K >= BK;
+}
+
+size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = choose_splits(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  SkinnyArgs p;
+  p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.a_block_rows = q.a_block_rows;
+  p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
+  p.nkb = (int)(q.K / BK);
+  p.sa_stride = (int)((q.M + q.a_block_rows - 1) / q.a_block_rows);
+  p.sb_stride = (int)((q.N + 127) / 128);
+  int S = choose_splits(q.M, q.N, q.K);
+  if (workspace == nullptr || workspace_bytes < skinny_workspace_bytes(q.M, q.N, q.K)) S = 1;
+  p.S = S;
+  p.partials = static_cast<float*>(workspace);
+  const unsigned grid = (unsigned)(((q.N + BN - 1) / BN) * S);
+  if (q.M <= 16)
+    hipLaunchKernelGGL(gemm_skinny_kernel<16>, dim3(grid), dim3(256), 0, stream, p);
+  else if (q.M <= 32)
+    hipLaunchKernelGGL(gemm_skinny_kernel<32>, dim3(grid), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_skinny_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace dg

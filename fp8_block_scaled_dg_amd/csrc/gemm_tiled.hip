@@ -22,9 +22,14 @@
 //    two LDS stages held in two distinct __shared__ arrays so that the
 //    compiler's LDS-DMA wait tracking can tell the stages apart.
 //  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which spreads the 16
-//    rows read by one MFMA fragment load over all banks.  The DMA writes stay
-//    linear (the permutation is applied to the global source addresses).
+//    c ^ x(r), x(r) = ((r & 3) << 1) ^ ((r >> 2) & 1).  This permutation was
+//    chosen by measurement (LDS bank-conflict counters on gfx950 over the
+//    exact fragment-read pattern, 16 rows x one chunk per 16-lane group, all
+//    four groups at different chunks of the same rows): it is conflict-free,
+//    while the XOR swizzles that merely give the 16 lanes distinct banks of a
+//    64 x 4-byte bank map are not.  The DMA writes stay linear (the
+//    permutation is applied to the global source addresses), so every 8
+//    consecutive lanes still fetch one full 128-byte row segment.
 //  * Workgroup ids are remapped so that each XCD (ids round-robin over 8
 //    XCDs) works on a contiguous, M-grouped patch of tiles that shares A and
 //    B panels in its own L2.
@@ -53,7 +58,7 @@ struct TiledArgs {
   int group_m;
 };
 
-__device__ __forceinline__ int lds_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+__device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 1); }
 
 // Stage one BK-wide slice of a ROWS x 128-byte operand tile into LDS.
 // Wave w issues ITERS instructions; instruction j fills LDS bytes
@@ -76,14 +81,17 @@ struct TileLoader {
     }
   }
 
+  __device__ __forceinline__ void issue_one(const uint8_t* base, uint8_t* lds, int wave, int kb,
+                                            int j) const {
+    const int cb = j * NW + wave;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(base + off[j] + (uint32_t)kb * BK),
+        (__attribute__((address_space(3))) void*)(lds + cb * 1024), 16, 0, 0);
+  }
+
   __device__ __forceinline__ void issue(const uint8_t* base, uint8_t* lds, int wave, int kb) const {
 #pragma unroll
-    for (int j = 0; j < ITERS; ++j) {
-      const int cb = j * NW + wave;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(base + off[j] + (uint32_t)kb * BK),
-          (__attribute__((address_space(3))) void*)(lds + cb * 1024), 16, 0, 0);
-    }
+    for (int j = 0; j < ITERS; ++j) issue_one(base, lds, wave, kb, j);
   }
 };
 
@@ -152,7 +160,7 @@ gemm_tiled_kernel(TiledArgs p) {
   lda.init(wave, lane, m0, p.M, p.K);
   ldb.init(wave, lane, n0, p.N, p.K);
 
-  // fragment read offsets (constant per lane: the swizzle depends on r % 16 only)
+  // fragment read offsets (constant per lane: the swizzle depends on r % 8 only)
   const int fr = lane & 15;
   const int off0 = fr * 128 + (((2 * (lane >> 4)) ^ lds_swz(fr)) * 16);
   const int off1 = fr * 128 + (((2 * (lane >> 4) + 1) ^ lds_swz(fr)) * 16);
@@ -195,8 +203,6 @@ gemm_tiled_kernel(TiledArgs p) {
     // The last step re-stages the final K slice into the idle buffer so the
     // body stays one basic block (the scheduling hints below need that).
     const int kn = kb + 1 < p.nkb ? kb + 1 : kb;
-    lda.issue(p.a, nxt, wave, kn);
-    ldb.issue(bbase, nxt + A_BYTES, wave, kn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sa_nxt[i] = p.sa[(int64_t)kn * p.sa_stride + sa_idx[i]];
     sb_nxt = sbbase[(int64_t)kn * p.sb_stride + nb];
@@ -212,8 +218,13 @@ gemm_tiled_kernel(TiledArgs p) {
     // 32 MFMAs in (j, i) order.  The 4 promotion FMAs of MFMA t are issued
     // after MFMA t+1, so they overlap the matrix core instead of stalling on
     // its result; the next B fragment is read right after the first MFMA of
-    // each group of four.  The fences pin this order against the scheduler,
-    // which otherwise hoists all MFMAs and parks 32 partials in registers.
+    // each group of four; the DMA instructions staging the next K step are
+    // spread one per two MFMAs over the first half (issued back to back they
+    // stall the wave on a full memory queue before its MFMAs can start).
+    // The fences pin this order against the scheduler, which otherwise
+    // hoists all MFMAs and parks 32 partials in registers.
+    constexpr int IA = TileLoader<BM, NW>::ITERS, IB = TileLoader<BN, NW>::ITERS;
+    static_assert(2 * (IA + IB) <= 32, "DMA issue slots");
     v4f part[2];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -222,6 +233,14 @@ gemm_tiled_kernel(TiledArgs p) {
       part[t & 1] =
           __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], zero, 0, 0, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if ((t & 1) == 0 && (t >> 1) < IA + IB) {
+        const int q = t >> 1;
+        if (q < IA)
+          lda.issue_one(p.a, nxt, wave, kn, q);
+        else
+          ldb.issue_one(bbase, nxt + A_BYTES, wave, kn, q - IA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (i == 0 && j < 7) {
         bf[(j + 1) & 1] = read_frag(cur + A_BYTES, wn * 128 + 16 * (j + 1), off0, off1);
         __builtin_amdgcn_sched_barrier(0);

@@ -161,3 +161,33 @@ def test_end_to_end_quantise_then_gemm(dg, orc):
     oqb, osb = orc.quantize(b, 128)
     ref = orc.gemm_nt(oqa, osa, oqb, osb, a_block_rows=128)
     assert_close(bf16_to_f64(c), ref, what="end-to-end")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 512), (5, 2056, 1024), (16, 136, 2048), (33, 1000, 640),
+                                   (64, 384, 4096), (64, 8192, 256), (2, 24576, 384)])
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_gemm_small_m_full_compare(dg, orc, M, N, K, use_ws):
+    """The small-M (decode) path, with and without the split-K workspace,
+    ragged N and K ranges that split unevenly, compared in full."""
+    qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=M * 7 + N)
+    ws = None
+    if use_ws:
+        nbytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=1)
+    c = bf16_to_f64(run_gemm(dg, qa, sa, qb, sb, 1, workspace=ws))
+    assert_close(c, ref, what="small-M %dx%dx%d ws=%s" % (M, N, K, use_ws))
+
+
+def test_gemm_small_m_split_k_deterministic_and_repeatable(dg, orc):
+    """Split-K sums partials in split order: repeated calls give identical bits
+    (the split-K counters are left zeroed by every call)."""
+    M, N, K = 16, 4096, 4096
+    qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=77)
+    nbytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    outs = [run_gemm(dg, qa, sa, qb, sb, 1, workspace=ws) for _ in range(3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=1)
+    assert_close(bf16_to_f64(outs[0]), ref, what="split-K repeat")
