@@ -4,22 +4,30 @@ Default workload (--config dense): the dense LLM projection GEMMs
 (M, N, K) in {(4096, 7168, 2048), (4096, 4096, 7168), (8192, 8192, 8192)},
 A ~ N(0, 1), B ~ N(0, 0.02^2), both quantised with 128x128 block scales,
 BF16 output.  One step = for every shape: quantise A (FP32 -> E4M3 + scales),
-quantise B, and the block-scaled GEMM, i.e. every stage of the path.  The
-inputs are resident in HBM before timing starts.
+quantise B, and the block-scaled GEMM -- every stage of the path.  Inputs are
+resident in HBM before timing starts.
 
-value = total GEMM FLOP of a step (2*M*N*K summed) / step time, in TFLOP/s.
+value = total GEMM FLOP of a step (2*M*N*K summed) / step time, TFLOP/s.
 
-Other workloads, each printing its own JSON line: --config decode (M in
-{1,16,64} x (N,K) in {(24576,1536),(7168,16384),(4096,4096)}, 1x128
-activation scales, weights rotated through buffers larger than the caches),
---config moe (8 experts, 1024 tokens top-2, up and down projections),
---config small (128x256x512).
+Timing: HIP events on the stream the kernels are launched on.  The steps are
+captured once into a HIP graph and replayed (every replay of the verification
+pass is checked bit for bit against the eager outputs), so host-side launch
+overhead of the Python binding does not count as GPU time; --no-graph times
+eager launches instead.
+
+Other workloads print their own JSON line: --config decode (M in {1,16,64} x
+(N,K) in {(24576,1536),(7168,16384),(4096,4096)}, 1x128 activation scales,
+weights rotated over > 768 MB of copies so the 256 MB Infinity Cache cannot
+hold them), --config moe (8 experts, 1024 tokens top-2, up and down
+projections), --config small (128x256x512), --config copy (a plain device
+copy of known size, used to calibrate the FETCH_SIZE/WRITE_SIZE counters).
 
 Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -36,6 +44,10 @@ import datagen  # noqa: E402
 
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+CSRC = os.path.join(ROOT, "fp8_block_scaled_dg_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+GEMM_TILED_SOURCES = ("gemm_tiled.hip", "dg_device.hpp")
 
 DENSE = [(4096, 7168, 2048), (4096, 4096, 7168), (8192, 8192, 8192)]
 DECODE = [(m, n, k) for (n, k) in [(24576, 1536), (7168, 16384), (4096, 4096)] for m in (1, 16, 64)]
@@ -49,30 +61,84 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class EventTimer:
-    """HIP events recorded on the stream the kernels are launched on."""
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
-    def __init__(self):
+
+def recorded_traffic(kernel_key: str, sources):
+    """HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE
+    (calibrated against a plain copy) and recorded in profiles/traffic.json,
+    valid only while the kernel sources still have the recorded hash."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(sources):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the launch stream; optionally over HIP-graph replays."""
+
+    def __init__(self, use_graph: bool):
         self.stream = torch.cuda.current_stream()
+        self.use_graph = use_graph
+        self.graphs = {}
 
-    def time(self, fn, reps: int) -> float:
-        """Average milliseconds per call over `reps` back-to-back calls."""
+    def graph(self, key, fn):
+        if key not in self.graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            torch.cuda.synchronize()
+            self.graphs[key] = g
+        return self.graphs[key]
+
+    def time(self, fn, reps: int, key=None, calls: int = 1) -> float:
+        """Milliseconds per call of fn (fn may enqueue several kernels).
+
+        With graphs, one graph holds `calls` back-to-back calls of fn, so that
+        the host cost of a replay is spread over enough GPU work to stay hidden
+        behind it (a single short kernel per replay would time the host)."""
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
-        s.record(self.stream)
-        for _ in range(reps):
+        if self.use_graph and key is not None:
+            def body():
+                for _ in range(calls):
+                    fn()
+            g = self.graph((key, calls), body)
+            g.replay()
+            torch.cuda.synchronize()
+            s.record(self.stream)
+            for _ in range(reps):
+                g.replay()
+            n = reps * calls
+        else:
             fn()
+            torch.cuda.synchronize()
+            s.record(self.stream)
+            for _ in range(reps):
+                fn()
+            n = reps
         e.record(self.stream)
         e.synchronize()
-        return s.elapsed_time(e) / reps
+        return s.elapsed_time(e) / n
 
 
 # ---------------------------------------------------------------------------
-# workloads
+# workloads.  Each has: rot (rotation states per graph), step(i), outputs(),
+# flops (per step), config(), breakdown(timer, reps), roofline(timer, reps),
+# cpu_baseline().
 # ---------------------------------------------------------------------------
 
 class Dense:
-    name = "dense"
+    rot = 1
 
     def __init__(self, dg, shapes, seed=0):
         self.dg = dg
@@ -80,13 +146,13 @@ class Dense:
         for (M, N, K) in shapes:
             a = torch.from_numpy(datagen.normal((M, K), 1.0, seed=seed, stream=0)).cuda()
             b = torch.from_numpy(datagen.normal((N, K), 0.02, seed=seed, stream=1)).cuda()
-            it = dict(M=M, N=N, K=K, a=a, b=b,
-                      qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
-                      qb=torch.empty((N, K), dtype=torch.uint8, device="cuda"),
-                      sa=torch.empty((K // 128, cdiv(M, 128)), dtype=torch.float32, device="cuda"),
-                      sb=torch.empty((K // 128, cdiv(N, 128)), dtype=torch.float32, device="cuda"),
-                      c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
-            self.items.append(it)
+            self.items.append(dict(
+                M=M, N=N, K=K, a=a, b=b,
+                qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
+                qb=torch.empty((N, K), dtype=torch.uint8, device="cuda"),
+                sa=torch.empty((K // 128, cdiv(M, 128)), dtype=torch.float32, device="cuda"),
+                sb=torch.empty((K // 128, cdiv(N, 128)), dtype=torch.float32, device="cuda"),
+                c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         self.flops = sum(2.0 * it["M"] * it["N"] * it["K"] for it in self.items)
 
     def quant_a(self, it):
@@ -98,11 +164,14 @@ class Dense:
     def gemm(self, it):
         self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], 128)
 
-    def step(self):
+    def step(self, i=0):
         for it in self.items:
             self.quant_a(it)
             self.quant_b(it)
             self.gemm(it)
+
+    def outputs(self):
+        return [t for it in self.items for t in (it["qa"], it["sa"], it["qb"], it["sb"], it["c"])]
 
     def config(self):
         return {"workload": "dense LLM projection GEMMs, E4M3 128x128 block scales, BF16 out",
@@ -113,39 +182,42 @@ class Dense:
 
     def breakdown(self, timer, reps):
         out = []
-        for it in self.items:
+        for n, it in enumerate(self.items):
             M, N, K = it["M"], it["N"], it["K"]
-            tq_a = timer.time(lambda: self.quant_a(it), reps)
-            tq_b = timer.time(lambda: self.quant_b(it), reps)
-            tg = timer.time(lambda: self.gemm(it), reps)
+            tq_a = timer.time(lambda: self.quant_a(it), reps, key=("qa", n), calls=10)
+            tq_b = timer.time(lambda: self.quant_b(it), reps, key=("qb", n), calls=10)
+            tg = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
             qbytes_a = M * K * 5 + 4 * (K // 128) * cdiv(M, 128)
             qbytes_b = N * K * 5 + 4 * (K // 128) * cdiv(N, 128)
             out.append({"mnk": [M, N, K],
                         "gemm_us": tg * 1e3, "gemm_tflops": 2.0 * M * N * K / (tg * 1e-3) / 1e12,
-                        "quant_a_us": tq_a * 1e3,
-                        "quant_a_gbs": qbytes_a / (tq_a * 1e-3) / 1e9,
-                        "quant_b_us": tq_b * 1e3,
-                        "quant_b_gbs": qbytes_b / (tq_b * 1e-3) / 1e9})
+                        "quant_a_us": tq_a * 1e3, "quant_a_gbs": qbytes_a / (tq_a * 1e-3) / 1e9,
+                        "quant_b_us": tq_b * 1e3, "quant_b_gbs": qbytes_b / (tq_b * 1e-3) / 1e9})
         return out
 
     def roofline(self, timer, reps):
-        """Dominant kernel: the GEMM launch on the largest shape."""
-        it = max(self.items, key=lambda t: t["M"] * t["N"] * t["K"])
-        t = timer.time(lambda: self.gemm(it), reps)
+        """Dominant kernel: the GEMM launch on the largest shape (8192^3)."""
+        n, it = max(enumerate(self.items), key=lambda t: t[1]["M"] * t[1]["N"] * t[1]["K"])
+        t = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
         flop = 2.0 * it["M"] * it["N"] * it["K"]
         ach = flop / (t * 1e-3) / 1e12
-        return {"kernel": "gemm_tiled_kernel<256,128,false> M=N=K=8192" if it["M"] == 8192 else
-                "gemm_tiled_kernel %s" % [it["M"], it["N"], it["K"]],
-                "bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_FP8_TFLOPS, "traffic": None, "avg_launch_us": t * 1e3}
+        key = "gemm_tiled_kernel<256,128,false> %dx%dx%d" % (it["M"], it["N"], it["K"])
+        return {"kernel": key, "bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_FP8_TFLOPS,
+                "traffic": recorded_traffic(key, GEMM_TILED_SOURCES),
+                "algorithmic_bytes": it["M"] * it["K"] + it["N"] * it["K"] + 2 * it["M"] * it["N"]
+                + 8 * (it["K"] // 128) * cdiv(it["M"], 128),
+                "avg_launch_us": t * 1e3}
 
     def cpu_baseline(self):
         """The oracle (single thread, plain C) on a bounded sample: per shape,
-        quantise all of B and one 128-row block of A, and compute one full
-        output row; extrapolate to the whole step (B quantised once, A in
+        quantise all of B and one 128-row block of A, and compute 4 full
+        output rows; extrapolated to the whole step (B quantised once, A in
         M/128 blocks, M output rows)."""
         import oracle
+        rows = 4
         total = 0.0
+        spent = 0.0
         for it in self.items:
             M, N, K = it["M"], it["N"], it["K"]
             a = datagen.normal((128, K), 1.0, seed=0, stream=0)
@@ -155,75 +227,86 @@ class Dense:
             t1 = time.perf_counter()
             qa, sa = oracle.quantize(a, 128)
             t2 = time.perf_counter()
-            oracle.gemm_nt_points(qa, sa, qb, sb, np.zeros(N, np.int64), np.arange(N),
-                                  a_block_rows=128)
+            ii = np.repeat(np.linspace(0, 127, rows).astype(np.int64), N)
+            jj = np.tile(np.arange(N, dtype=np.int64), rows)
+            oracle.gemm_nt_points(qa, sa, qb, sb, ii, jj, a_block_rows=128)
             t3 = time.perf_counter()
-            total += (t1 - t0) + (M / 128) * (t2 - t1) + M * (t3 - t2)
+            spent += t3 - t0
+            total += (t1 - t0) + (M / 128) * (t2 - t1) + (M / rows) * (t3 - t2)
         return {"value": self.flops / total / 1e12, "unit": "TFLOP/s", "cores": 1,
                 "kind": "oracle",
                 "sample": "per shape: oracle quantise of all of B and one 128-row block of A, "
-                          "one full output row of the FP64 dequantised GEMM; extrapolated to "
-                          "the full step (%.1f s extrapolated)" % total}
+                          "%d full output rows of the FP64 dequantised GEMM (%.1f s of CPU "
+                          "time); extrapolated to the full step (%.0f s)" % (rows, spent, total)}
 
 
 class Decode:
-    name = "decode"
-
     def __init__(self, dg, rotate_bytes=768 << 20, seed=0):
         self.dg = dg
         self.items = []
         for (M, N, K) in DECODE:
-            wbytes = N * K
-            copies = max(2, cdiv(rotate_bytes, wbytes))
-            qb = torch.randint(0, 0x7E, (copies, N, K), dtype=torch.uint8, device="cuda")
-            sb = torch.rand((copies, K // 128, N // 128), device="cuda") * 1e-3
+            copies = max(2, cdiv(rotate_bytes, N * K))
+            g = torch.Generator(device="cuda")
+            g.manual_seed(seed + M * 7 + N)
+            qb = torch.randint(0, 0x7E, (copies, N, K), dtype=torch.uint8, device="cuda",
+                               generator=g)
+            sb = torch.rand((copies, K // 128, N // 128), device="cuda", generator=g) * 1e-3
             a = torch.from_numpy(datagen.normal((M, K), 1.0, seed=seed, stream=M)).cuda()
-            qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
-            sa = torch.empty((K // 128, M), dtype=torch.float32, device="cuda")
             ws_bytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-            c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-            self.items.append(dict(M=M, N=N, K=K, qb=qb, sb=sb, a=a, qa=qa, sa=sa, c=c, ws=ws,
-                                   copies=copies, i=0))
+            self.items.append(dict(
+                M=M, N=N, K=K, qb=qb, sb=sb, a=a, copies=copies,
+                qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
+                sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
+                ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda"),
+                c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+        self.rot = max(it["copies"] for it in self.items)
         self.flops = sum(2.0 * it["M"] * it["N"] * it["K"] for it in self.items)
 
-    def gemm(self, it):
-        i = it["i"]
-        it["i"] = (i + 1) % it["copies"]
-        self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"][i], it["sa"], it["sb"][i], 1,
+    @staticmethod
+    def bytes_of(it):
+        M, N, K = it["M"], it["N"], it["K"]
+        return N * K + M * K + 4 * (K // 128) * (M + N // 128) + 2 * M * N
+
+    def gemm(self, it, i):
+        j = i % it["copies"]
+        self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"][j], it["sa"], it["sb"][j], 1,
                                workspace=it["ws"])
 
-    def quant(self, it):
-        self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
-
-    def step(self):
+    def step(self, i=0):
         for it in self.items:
-            self.quant(it)
-            self.gemm(it)
+            self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
+            self.gemm(it, i)
+
+    def outputs(self):
+        return [t for it in self.items for t in (it["qa"], it["sa"], it["c"])]
 
     def config(self):
         return {"workload": "decode-shaped GEMMs, M in {1,16,64} x (N,K) in {(24576,1536),"
                             "(7168,16384),(4096,4096)}, A 1x128 scales, B 128x128 scales",
                 "step": "quantise A + GEMM per shape; weights rotated over >768 MB of copies"}
 
+    def _time_gemm(self, timer, n, it, reps):
+        rot = it["copies"]
+        return timer.time(lambda: [self.gemm(it, i) for i in range(rot)], reps,
+                          key=("dec", n)) / rot
+
     def breakdown(self, timer, reps):
         out = []
-        for it in self.items:
-            M, N, K = it["M"], it["N"], it["K"]
-            t = timer.time(lambda: self.gemm(it), reps)
-            byts = N * K + M * K + 4 * (K // 128) * (M + N // 128) + 2 * M * N
-            out.append({"mnk": [M, N, K], "gemm_us": t * 1e3, "hbm_gbs": byts / (t * 1e-3) / 1e9,
-                        "hbm_frac": byts / (t * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        for n, it in enumerate(self.items):
+            t = self._time_gemm(timer, n, it, reps)
+            b = self.bytes_of(it)
+            out.append({"mnk": [it["M"], it["N"], it["K"]], "gemm_us": t * 1e3,
+                        "hbm_gbs": b / (t * 1e-3) / 1e9,
+                        "hbm_frac": b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS})
         return out
 
     def roofline(self, timer, reps):
-        it = max(self.items, key=lambda t: t["N"] * t["K"] * 1000 + t["M"])
-        t = timer.time(lambda: self.gemm(it), reps)
-        M, N, K = it["M"], it["N"], it["K"]
-        byts = N * K + M * K + 4 * (K // 128) * (M + N // 128) + 2 * M * N
-        ach = byts / (t * 1e-3) / 1e9
-        return {"kernel": "decode GEMM %s" % [M, N, K], "bound": "hbm", "achieved": ach,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+        n, it = max(enumerate(self.items), key=lambda t: t[1]["N"] * t[1]["K"] * 1000 + t[1]["M"])
+        t = self._time_gemm(timer, n, it, reps)
+        b = self.bytes_of(it)
+        ach = b / (t * 1e-3) / 1e9
+        return {"kernel": "decode GEMM %s" % [it["M"], it["N"], it["K"]], "bound": "hbm",
+                "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                 "traffic": None, "avg_launch_us": t * 1e3}
 
     def cpu_baseline(self):
@@ -231,7 +314,7 @@ class Decode:
 
 
 class Moe:
-    name = "moe"
+    rot = 1
 
     def __init__(self, dg, seed=0):
         self.dg = dg
@@ -241,25 +324,31 @@ class Moe:
         M = mi.shape[0]
         self.real_rows = int((r["m_indices"] >= 0).sum())
         self.items = []
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
         for (N, K) in ((I, H), (H, I)):
-            qb = torch.randint(0, 0x7E, (G, N, K), dtype=torch.uint8, device="cuda")
-            sb = torch.rand((G, K // 128, N // 128), device="cuda") * 1e-3
+            qb = torch.randint(0, 0x7E, (G, N, K), dtype=torch.uint8, device="cuda", generator=gen)
+            sb = torch.rand((G, K // 128, N // 128), device="cuda", generator=gen) * 1e-3
             a = torch.from_numpy(datagen.normal((M, K), 1.0, seed=seed, stream=K)).cuda()
             a[mi < 0] = 0
-            self.items.append(dict(M=M, N=N, K=K, qb=qb, sb=sb, a=a, mi=mi,
-                                   qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
-                                   sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
-                                   c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+            self.items.append(dict(
+                M=M, N=N, K=K, qb=qb, sb=sb, a=a, mi=mi,
+                qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
+                sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
+                c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         self.flops = sum(2.0 * self.real_rows * it["N"] * it["K"] for it in self.items)
 
     def gemm(self, it):
         self.dg.dg_fp8_grouped_gemm_contig(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], 1,
                                            it["mi"])
 
-    def step(self):
+    def step(self, i=0):
         for it in self.items:
             self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
             self.gemm(it)
+
+    def outputs(self):
+        return [t for it in self.items for t in (it["qa"], it["sa"], it["c"])]
 
     def config(self):
         return {"workload": "grouped MoE GEMM, M-contiguous, 8 experts, 1024 tokens top-2, "
@@ -268,17 +357,18 @@ class Moe:
 
     def breakdown(self, timer, reps):
         out = []
-        for it in self.items:
-            t = timer.time(lambda: self.gemm(it), reps)
+        for n, it in enumerate(self.items):
+            t = timer.time(lambda: self.gemm(it), reps, key=("moe", n), calls=4)
             byts = 8 * it["N"] * it["K"] + it["M"] * it["K"] + 2 * it["M"] * it["N"]
             out.append({"nk": [it["N"], it["K"]], "gemm_us": t * 1e3,
-                        "tflops_real_rows": 2.0 * self.real_rows * it["N"] * it["K"] / (t * 1e-3) / 1e12,
+                        "tflops_real_rows": 2.0 * self.real_rows * it["N"] * it["K"]
+                        / (t * 1e-3) / 1e12,
                         "hbm_gbs": byts / (t * 1e-3) / 1e9})
         return out
 
     def roofline(self, timer, reps):
         it = self.items[0]
-        t = timer.time(lambda: self.gemm(it), reps)
+        t = timer.time(lambda: self.gemm(it), reps, key=("moe", 0), calls=4)
         byts = 8 * it["N"] * it["K"] + it["M"] * it["K"] + 2 * it["M"] * it["N"]
         ach = byts / (t * 1e-3) / 1e9
         return {"kernel": "grouped GEMM up-projection", "bound": "hbm", "achieved": ach,
@@ -289,13 +379,36 @@ class Moe:
         return None
 
 
+def run_copy(args):
+    """A plain device-to-device copy of known size (for counter calibration)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e.record()
+    e.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"metric": "device copy bandwidth (read+write)", "bytes_read": n,
+                      "bytes_written": n, "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                      "ms_per_copy": ms, "n_gpus": 1, "steps": args.steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="dense", choices=["dense", "decode", "moe", "small"])
+    ap.add_argument("--config", default="dense",
+                    choices=["dense", "decode", "moe", "small", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -305,9 +418,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.config == "copy":
+        run_copy(args)
+        return
 
     import fp8_block_scaled_dg_amd as dg
-    torch.cuda.set_device(0)
     log("building inputs for", args.config)
     if args.config == "dense":
         w = Dense(dg, DENSE)
@@ -320,16 +436,42 @@ def main():
     torch.cuda.synchronize()
 
     log("warmup", args.warmup)
-    for _ in range(args.warmup):
-        w.step()
+    for i in range(args.warmup):
+        w.step(i)
     torch.cuda.synchronize()
-    log("timing", args.steps, "steps")
-    timer = EventTimer()
+
+    use_graph = not args.no_graph
+    timer = Timer(use_graph)
+    rounds = args.steps
+    if use_graph:
+        # one graph = w.rot consecutive steps (rotation states); verify replays
+        eager = []
+        for i in range(w.rot):
+            w.step(i)
+        torch.cuda.synchronize()
+        eager = [t.clone() for t in w.outputs()]
+        g = timer.graph("step", lambda: [w.step(i) for i in range(w.rot)])
+        for _ in range(3):
+            for t in w.outputs():
+                t.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(x, y) for x, y in zip(w.outputs(), eager)):
+                log("graph replay differs from eager execution: timing eager launches")
+                use_graph = False
+                timer = Timer(False)
+                break
+        rounds = cdiv(args.steps, w.rot)
+    steps = rounds * w.rot if use_graph else args.steps
+    log("timing", steps, "steps", "(graph)" if use_graph else "(eager)")
     t0 = time.perf_counter()
-    ms = timer.time(w.step, args.steps)
-    torch.cuda.synchronize()
+    if use_graph:
+        ms = timer.time(lambda: [w.step(i) for i in range(w.rot)], rounds, key="step") / w.rot
+    else:
+        ms = timer.time(w.step, steps)
     wall = time.perf_counter() - t0
-    log("step %.3f ms (wall %.2f s)" % (ms, wall))
+    log("step %.4f ms (wall %.2f s)" % (ms, wall))
 
     breakdown = w.breakdown(timer, args.kernel_reps)
     roof = w.roofline(timer, args.kernel_reps)
@@ -340,11 +482,11 @@ def main():
         cpu = w.cpu_baseline()
 
     rec = {"metric": "FP8 block-scaled GEMM TFLOPS", "value": w.flops / (ms * 1e-3) / 1e12,
-           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
-           "config": w.config(), "roofline": roof, "cpu_baseline": cpu,
-           "breakdown": breakdown}
+           "config": dict(w.config(), timing="hip graph replay" if use_graph else "eager"),
+           "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown}
     print(json.dumps(rec), flush=True)
 
 
