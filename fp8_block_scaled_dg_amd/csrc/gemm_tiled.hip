@@ -36,11 +36,16 @@
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
+#include <stdlib.h>
+
 namespace dg {
 namespace {
 
 constexpr int BN = 256;
 constexpr int BK = 128;
+
+// s_waitcnt immediate: vmcnt(4), expcnt and lgkmcnt left at their maxima.
+constexpr int kVmcnt4 = 4 | (7 << 4) | (15 << 8);
 
 struct TiledArgs {
   uint16_t* c;
@@ -89,6 +94,19 @@ struct TileLoader {
         (__attribute__((address_space(3))) void*)(lds + cb * 1024), 16, 0, 0);
   }
 
+  // base + koff is the (uniform) start of the K block; the empty asm hides the
+  // lane offset from loop strength reduction, which would otherwise keep one
+  // pointer per (instruction, unrolled step) live
+  __device__ __forceinline__ void issue_at(const uint8_t* base, uint32_t koff, uint8_t* lds,
+                                           int wave, int j) const {
+    const int cb = j * NW + wave;
+    uint32_t o = off[j];
+    asm volatile("" : "+v"(o));
+    __builtin_amdgcn_global_load_lds((const void*)(base + (o + koff)),
+                                     (__attribute__((address_space(3))) void*)(lds + cb * 1024),
+                                     16, 0, 0);
+  }
+
   __device__ __forceinline__ void issue(const uint8_t* base, uint8_t* lds, int wave, int kb) const {
 #pragma unroll
     for (int j = 0; j < ITERS; ++j) issue_one(base, lds, wave, kb, j);
@@ -117,6 +135,49 @@ __device__ __forceinline__ void map_tile(const TiledArgs& p, int& tm, int& tn) {
   tn = rem / gsz;
 }
 
+// Grouped tiles are indexed by 128-row block.  Every block carries one expert
+// id (rows of an expert are contiguous and padded to 128).  The blocks of one
+// expert are paired: the first block of each pair computes a 256-row tile,
+// the second has nothing to do, and an odd block left at the end of an
+// expert's run computes 128 rows (the loads and MFMAs of the other half are
+// spent on clamped rows that are never stored).  A block whose first row is
+// padding (id -1) is all padding: its workgroup writes zeros.  Returns false
+// when the workgroup has nothing more to do.
+__device__ __forceinline__ bool grouped_tile(const TiledArgs& p, int blk, int n0, int lane,
+                                             int& m0, int& rows_end, const uint8_t*& bbase,
+                                             const float*& sbbase) {
+  m0 = blk * 128;
+  const int g = p.m_indices[m0];
+  if (g < 0 || g >= p.num_groups) {
+    for (int idx = threadIdx.x; idx < 128 * (BN / 8); idx += blockDim.x) {
+      const int r = idx / (BN / 8);
+      const int cc = (idx % (BN / 8)) * 8;
+      if (n0 + cc < p.N)
+        *reinterpret_cast<uint4*>(p.c + (int64_t)(m0 + r) * p.N + n0 + cc) = make_uint4(0, 0, 0, 0);
+    }
+    return false;
+  }
+  // first block of the run of blocks with id g that ends at blk: each lane
+  // looks at one earlier block, 64 blocks per round
+  int start = 0;
+  for (int base = blk;; base -= 64) {
+    const int bb = base - 1 - lane;
+    const bool differs = bb < 0 || p.m_indices[(int64_t)bb * 128] != g;
+    const unsigned long long mask = __ballot(differs);
+    if (mask != 0ull) {
+      start = base - (__ffsll(mask) - 1);
+      break;
+    }
+  }
+  if ((blk - start) & 1) return false;  // covered by the tile of the previous block
+  const int nblk = p.M / 128;
+  const bool pair = blk + 1 < nblk && p.m_indices[(int64_t)(blk + 1) * 128] == g;
+  rows_end = m0 + (pair ? 256 : 128);
+  bbase += (int64_t)g * p.N * p.K;
+  sbbase += (int64_t)g * p.nkb * p.sb_stride;
+  return true;
+}
+
 template <int BM, int A_BLK, bool GROUPED>
 __global__ void __launch_bounds__(BM * BN / 128)
 gemm_tiled_kernel(TiledArgs p) {
@@ -128,36 +189,25 @@ gemm_tiled_kernel(TiledArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int wm = wave % WM;
   const int wn = wave / WM;
 
   int tm, tn;
   map_tile(p, tm, tn);
-  const int m0 = tm * BM;
   const int n0 = tn * BN;
+  int m0 = tm * BM;
+  int rows_end = p.M;  // rows [m0, rows_end) are stored
 
   const uint8_t* bbase = p.b;
   const float* sbbase = p.sb;
   if (GROUPED) {
-    const int g = p.m_indices[m0];
-    if (g < 0 || g >= p.num_groups) {
-      // whole block is padding: zero rows
-      for (int idx = threadIdx.x; idx < BM * (BN / 8); idx += NW * 64) {
-        const int r = idx / (BN / 8);
-        const int cc = (idx % (BN / 8)) * 8;
-        if (n0 + cc < p.N)
-          *reinterpret_cast<uint4*>(p.c + (int64_t)(m0 + r) * p.N + n0 + cc) = make_uint4(0, 0, 0, 0);
-      }
-      return;
-    }
-    bbase += (int64_t)g * p.N * p.K;
-    sbbase += (int64_t)g * p.nkb * p.sb_stride;
+    if (!grouped_tile(p, tm, n0, lane, m0, rows_end, bbase, sbbase)) return;
   }
 
   TileLoader<BM, NW> lda;
   TileLoader<BN, NW> ldb;
-  lda.init(wave, lane, m0, p.M, p.K);
+  lda.init(wave, lane, m0, rows_end, p.K);
   ldb.init(wave, lane, n0, p.N, p.K);
 
   // fragment read offsets (constant per lane: the swizzle depends on r % 8 only)
@@ -171,7 +221,7 @@ gemm_tiled_kernel(TiledArgs p) {
   for (int i = 0; i < 4; ++i) {
     int m = m0 + wm * 64 + 16 * i + fr;
     if (A_BLK == 1) {
-      sa_idx[i] = m < p.M ? m : p.M - 1;
+      sa_idx[i] = m < rows_end ? m : rows_end - 1;
     } else {
       int rb = (m0 + wm * 64) / 128;
       sa_idx[i] = rb < p.sa_stride ? rb : p.sa_stride - 1;
@@ -270,7 +320,7 @@ gemm_tiled_kernel(TiledArgs p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + wm * 64 + 16 * i + fr;
-    if (m >= p.M) continue;
+    if (m >= rows_end) continue;
     bool zero_row = false;
     if (GROUPED) zero_row = p.m_indices[m] < 0;
 #pragma unroll
@@ -290,7 +340,186 @@ gemm_tiled_kernel(TiledArgs p) {
   }
 }
 
-template <int BM, int A_BLK, bool GROUPED>
+// 256 x 256 tile with a five-slot LDS ring of half stages, for operands that
+// stream from HBM (grouped MoE weights), where one stage of lookahead does not
+// cover the memory latency.
+//
+// A half stage is one 32 KB operand slice (A or B, 256 rows x 128 K bytes);
+// the 160 KB of LDS hold five of them.  Step k reads A_k and B_k from slots
+// 2k mod 5 and 2k+1 mod 5 while the DMA for B_{k+1} and A_{k+2} streams into
+// the two slots that step k-1 released, one DMA instruction per four MFMAs, so
+// every slice is requested one to two steps before it is read.  At the top of
+// step k every slice except the most recent (A_{k+1}) must have landed:
+// s_waitcnt vmcnt(4), then one barrier, which also certifies that all waves
+// have finished reading the slots about to be refilled.
+template <int A_BLK, bool GROUPED>
+__global__ void __launch_bounds__(512)
+gemm_ring_kernel(TiledArgs p) {
+  constexpr int BM = 256;
+  constexpr int WM = 4;
+  constexpr int NW = 8;
+  constexpr int HALF = 256 * BK;
+  __shared__ __attribute__((aligned(1024))) uint8_t r0[HALF];
+  __shared__ __attribute__((aligned(1024))) uint8_t r1[HALF];
+  __shared__ __attribute__((aligned(1024))) uint8_t r2[HALF];
+  __shared__ __attribute__((aligned(1024))) uint8_t r3[HALF];
+  __shared__ __attribute__((aligned(1024))) uint8_t r4[HALF];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+
+  int tm, tn;
+  map_tile(p, tm, tn);
+  const int n0 = tn * BN;
+  int m0 = tm * BM;
+  int rows_end = p.M;
+  const uint8_t* bbase = p.b;
+  const float* sbbase = p.sb;
+  if (GROUPED) {
+    if (!grouped_tile(p, tm, n0, lane, m0, rows_end, bbase, sbbase)) return;
+  }
+
+  TileLoader<BM, NW> lda;
+  TileLoader<BN, NW> ldb;
+  lda.init(wave, lane, m0, rows_end, p.K);
+  ldb.init(wave, lane, n0, p.N, p.K);
+
+  const int fr = lane & 15;
+  const int off0 = fr * 128 + (((2 * (lane >> 4)) ^ lds_swz(fr)) * 16);
+  const int off1 = fr * 128 + (((2 * (lane >> 4) + 1) ^ lds_swz(fr)) * 16);
+
+  int sa_idx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int m = m0 + wm * 64 + 16 * i + fr;
+    if (A_BLK == 1) {
+      sa_idx[i] = m < rows_end ? m : rows_end - 1;
+    } else {
+      int rb = (m0 + wm * 64) / 128;
+      sa_idx[i] = rb < p.sa_stride ? rb : p.sa_stride - 1;
+    }
+  }
+  int nb = (n0 + wn * 128) / 128;
+  nb = nb < p.sb_stride ? nb : p.sb_stride - 1;
+  const int last = p.nkb - 1;
+
+  v4f acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // The scales of block k are loaded during step k-1 (block 0 here) and their
+  // products formed at the top of step k, after the wait that covers them.
+  float sa_nxt[4];
+  float sb_nxt = sbbase[nb];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sa_nxt[i] = p.sa[sa_idx[i]];
+
+  // prologue: A_0, B_0, A_1 (A_1 re-reads block 0 when K has one block)
+  lda.issue(p.a, r0, wave, 0);
+  ldb.issue(bbase, r1, wave, 0);
+  lda.issue(p.a, r2, wave, last > 0 ? 1 : 0);
+
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](const uint8_t* a_l, const uint8_t* b_l, uint8_t* wb, uint8_t* wa, int kb) {
+    __builtin_amdgcn_s_waitcnt(kVmcnt4);
+    asm volatile("s_barrier" ::: "memory");
+    float s_cur[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_cur[i] = sa_nxt[i] * sb_nxt;
+    // uniform per-step block indices (readfirstlane keeps the compiler from
+    // deriving one pointer induction variable per unrolled step)
+    const int k1 = __builtin_amdgcn_readfirstlane(kb + 1 < last ? kb + 1 : last);
+    const int k2 = __builtin_amdgcn_readfirstlane(kb + 2 < last ? kb + 2 : last);
+    const float* sa_row = p.sa + (int64_t)k1 * p.sa_stride;
+    const float* sb_row = sbbase + (int64_t)k1 * p.sb_stride;
+    const uint32_t kb1 = (uint32_t)k1 * BK, kb2 = (uint32_t)k2 * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t o = (uint32_t)sa_idx[i] * 4u;
+      asm volatile("" : "+v"(o));
+      sa_nxt[i] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sa_row) + o);
+    }
+    sb_nxt = sb_row[nb];
+
+    v8i af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = read_frag(a_l, wm * 64 + 16 * i, off0, off1);
+    v8i bf[2];
+    bf[0] = read_frag(b_l, wn * 128, off0, off1);
+    v4f part[2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int j = t >> 2, i = t & 3;
+      part[t & 1] =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], zero, 0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((t & 3) == 1) {
+        const int q = t >> 2;  // B_{k+1} parts 0..3, then A_{k+2} parts 0..3
+        if (q < 4)
+          ldb.issue_at(bbase, kb1, wb, wave, q);
+        else
+          lda.issue_at(p.a, kb2, wa, wave, q - 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i == 0 && j < 7) {
+        bf[(j + 1) & 1] = read_frag(b_l, wn * 128 + 16 * (j + 1), off0, off1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (t > 0) {
+        const int tp = t - 1, jp = tp >> 2, ip = tp & 3;
+        acc[ip][jp] += part[tp & 1] * s_cur[ip];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    acc[3][7] += part[1] * s_cur[3];
+  };
+
+  // A_k sits in slot 2k mod 5 and B_k in 2k+1 mod 5: the pattern repeats
+  // every five steps
+  int kb = 0;
+  for (; kb + 5 <= p.nkb; kb += 5) {
+    step(r0, r1, r3, r4, kb);
+    step(r2, r3, r0, r1, kb + 1);
+    step(r4, r0, r2, r3, kb + 2);
+    step(r1, r2, r4, r0, kb + 3);
+    step(r3, r4, r1, r2, kb + 4);
+  }
+  if (kb < p.nkb) step(r0, r1, r3, r4, kb);
+  if (kb + 1 < p.nkb) step(r2, r3, r0, r1, kb + 1);
+  if (kb + 2 < p.nkb) step(r4, r0, r2, r3, kb + 2);
+  if (kb + 3 < p.nkb) step(r1, r2, r4, r0, kb + 3);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 64 + 16 * i + fr;
+    if (m >= rows_end) continue;
+    bool zero_row = false;
+    if (GROUPED) zero_row = p.m_indices[m] < 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
+      if (n < p.N) {
+        uint2 v;
+        if (zero_row) {
+          v = make_uint2(0, 0);
+        } else {
+          v.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+          v.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        }
+        *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = v;
+      }
+    }
+  }
+}
+
+template <bool RING, int A_BLK, bool GROUPED>
 hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   TiledArgs p;
   p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
@@ -299,24 +528,41 @@ hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   p.nkb = (int)(q.K / BK);
   p.sa_stride = (int)((q.M + q.a_block_rows - 1) / q.a_block_rows);
   p.sb_stride = (int)((q.N + 127) / 128);
-  p.tiles_m = (int)((q.M + BM - 1) / BM);
+  p.tiles_m = GROUPED ? (int)(q.M / 128) : (int)((q.M + 255) / 256);
   p.tiles_n = (int)((q.N + BN - 1) / BN);
-  p.group_m = GROUPED ? 2 : 4;
+  p.group_m = 4;
   const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, A_BLK, GROUPED>), dim3(grid), dim3(BM * BN / 128),
-                     0, stream, p);
+  if (RING)
+    hipLaunchKernelGGL((gemm_ring_kernel<A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_tiled_kernel<256, A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream,
+                       p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Kernel choice (DG_TILED=pair|ring overrides it, read once, for tuning): the
+// two-stage kernel for dense operands, which mostly hit in L2; the ring for
+// grouped weights, which stream from HBM.
 hipError_t launch_gemm_tiled(const GemmProblem& q, bool grouped, hipStream_t stream) {
+  static const int forced = [] {
+    const char* e = getenv("DG_TILED");
+    return e ? (e[0] == 'p' ? 1 : (e[0] == 'r' ? 2 : 0)) : 0;
+  }();
+  const bool ring = forced ? forced == 2 : grouped;
   if (grouped) {
-    return q.a_block_rows == 1 ? launch_one<128, 1, true>(q, stream)
-                               : launch_one<128, 128, true>(q, stream);
+    if (ring)
+      return q.a_block_rows == 1 ? launch_one<true, 1, true>(q, stream)
+                                 : launch_one<true, 128, true>(q, stream);
+    return q.a_block_rows == 1 ? launch_one<false, 1, true>(q, stream)
+                               : launch_one<false, 128, true>(q, stream);
   }
-  return q.a_block_rows == 1 ? launch_one<256, 1, false>(q, stream)
-                             : launch_one<256, 128, false>(q, stream);
+  if (ring)
+    return q.a_block_rows == 1 ? launch_one<true, 1, false>(q, stream)
+                               : launch_one<true, 128, false>(q, stream);
+  return q.a_block_rows == 1 ? launch_one<false, 1, false>(q, stream)
+                             : launch_one<false, 128, false>(q, stream);
 }
 
 }  // namespace dg
