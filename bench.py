@@ -19,8 +19,10 @@ Other workloads print their own JSON line: --config decode (M in {1,16,64} x
 (N,K) in {(24576,1536),(7168,16384),(4096,4096)}, 1x128 activation scales,
 weights rotated over > 768 MB of copies so the 256 MB Infinity Cache cannot
 hold them), --config moe (8 experts, 1024 tokens top-2, up and down
-projections), --config small (128x256x512), --config copy (a plain device
-copy of known size, used to calibrate the FETCH_SIZE/WRITE_SIZE counters).
+projections), --config small (128x256x512), --config outlier (8192^3 with
+heavy-tailed, hot-channel activations and 1x128 activation scales),
+--config copy (a plain device copy of known size, used to calibrate the
+FETCH_SIZE/WRITE_SIZE counters).
 
 Prints ONE JSON line on stdout.
 """
@@ -140,29 +142,37 @@ class Timer:
 class Dense:
     rot = 1
 
-    def __init__(self, dg, shapes, seed=0):
+    def __init__(self, dg, shapes, seed=0, outlier=False):
+        """outlier: A = heavy-tailed rows with 1% hot channels x100, quantised
+        with 1x128 (per-row) scales; otherwise A ~ N(0,1) with 128x128 scales."""
         self.dg = dg
+        self.outlier = outlier
+        self.a_br = 1 if outlier else 128
         self.items = []
         for (M, N, K) in shapes:
-            a = torch.from_numpy(datagen.normal((M, K), 1.0, seed=seed, stream=0)).cuda()
+            if outlier:
+                a_np, _ = datagen.student_t_outliers(M, K, seed=seed, stream=5)
+            else:
+                a_np = datagen.normal((M, K), 1.0, seed=seed, stream=0)
+            a = torch.from_numpy(a_np).cuda()
             b = torch.from_numpy(datagen.normal((N, K), 0.02, seed=seed, stream=1)).cuda()
             self.items.append(dict(
                 M=M, N=N, K=K, a=a, b=b,
                 qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
                 qb=torch.empty((N, K), dtype=torch.uint8, device="cuda"),
-                sa=torch.empty((K // 128, cdiv(M, 128)), dtype=torch.float32, device="cuda"),
+                sa=torch.empty((K // 128, cdiv(M, self.a_br)), dtype=torch.float32, device="cuda"),
                 sb=torch.empty((K // 128, cdiv(N, 128)), dtype=torch.float32, device="cuda"),
                 c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         self.flops = sum(2.0 * it["M"] * it["N"] * it["K"] for it in self.items)
 
     def quant_a(self, it):
-        self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 128)
+        self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], self.a_br)
 
     def quant_b(self, it):
         self.dg.dg_quantize_fp8_block(it["qb"], it["sb"], it["b"], 128)
 
     def gemm(self, it):
-        self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], 128)
+        self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], self.a_br)
 
     def step(self, i=0):
         for it in self.items:
@@ -174,6 +184,13 @@ class Dense:
         return [t for it in self.items for t in (it["qa"], it["sa"], it["qb"], it["sb"], it["c"])]
 
     def config(self):
+        if self.outlier:
+            return {"workload": "outlier activations: 8192^3 GEMM, A heavy-tailed (Student-t, "
+                                "nu=3) with 1% hot channels x100, 1x128 A scales",
+                    "shapes_mnk": [[it["M"], it["N"], it["K"]] for it in self.items],
+                    "a_scales": "1x128", "b_scales": "128x128",
+                    "step": "quantise A + quantise B + GEMM",
+                    "inputs": "B ~ N(0,0.02^2), float32, seed 0"}
         return {"workload": "dense LLM projection GEMMs, E4M3 128x128 block scales, BF16 out",
                 "shapes_mnk": [[it["M"], it["N"], it["K"]] for it in self.items],
                 "a_scales": "128x128", "b_scales": "128x128",
@@ -187,7 +204,7 @@ class Dense:
             tq_a = timer.time(lambda: self.quant_a(it), reps, key=("qa", n), calls=10)
             tq_b = timer.time(lambda: self.quant_b(it), reps, key=("qb", n), calls=10)
             tg = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
-            qbytes_a = M * K * 5 + 4 * (K // 128) * cdiv(M, 128)
+            qbytes_a = M * K * 5 + 4 * (K // 128) * cdiv(M, self.a_br)
             qbytes_b = N * K * 5 + 4 * (K // 128) * cdiv(N, 128)
             out.append({"mnk": [M, N, K],
                         "gemm_us": tg * 1e3, "gemm_tflops": 2.0 * M * N * K / (tg * 1e-3) / 1e12,
@@ -201,12 +218,12 @@ class Dense:
         t = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
         flop = 2.0 * it["M"] * it["N"] * it["K"]
         ach = flop / (t * 1e-3) / 1e12
-        key = "gemm_tiled_kernel<256,128,false> %dx%dx%d" % (it["M"], it["N"], it["K"])
+        key = "gemm_tiled_kernel<256,%d,false> %dx%dx%d" % (self.a_br, it["M"], it["N"], it["K"])
         return {"kernel": key, "bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_FP8_TFLOPS,
                 "traffic": recorded_traffic(key, GEMM_TILED_SOURCES),
                 "algorithmic_bytes": it["M"] * it["K"] + it["N"] * it["K"] + 2 * it["M"] * it["N"]
-                + 8 * (it["K"] // 128) * cdiv(it["M"], 128),
+                + 4 * (it["K"] // 128) * (cdiv(it["M"], self.a_br) + cdiv(it["N"], 128)),
                 "avg_launch_us": t * 1e3}
 
     def cpu_baseline(self):
@@ -220,16 +237,16 @@ class Dense:
         spent = 0.0
         for it in self.items:
             M, N, K = it["M"], it["N"], it["K"]
-            a = datagen.normal((128, K), 1.0, seed=0, stream=0)
+            a = it["a"][:128].cpu().numpy()
             b = it["b"].cpu().numpy()
             t0 = time.perf_counter()
             qb, sb = oracle.quantize(b, 128)
             t1 = time.perf_counter()
-            qa, sa = oracle.quantize(a, 128)
+            qa, sa = oracle.quantize(a, self.a_br)
             t2 = time.perf_counter()
             ii = np.repeat(np.linspace(0, 127, rows).astype(np.int64), N)
             jj = np.tile(np.arange(N, dtype=np.int64), rows)
-            oracle.gemm_nt_points(qa, sa, qb, sb, ii, jj, a_block_rows=128)
+            oracle.gemm_nt_points(qa, sa, qb, sb, ii, jj, a_block_rows=self.a_br)
             t3 = time.perf_counter()
             spent += t3 - t0
             total += (t1 - t0) + (M / 128) * (t2 - t1) + (M / rows) * (t3 - t2)
@@ -406,7 +423,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="dense",
-                    choices=["dense", "decode", "moe", "small", "copy"])
+                    choices=["dense", "decode", "moe", "small", "outlier", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -429,6 +446,8 @@ def main():
         w = Dense(dg, DENSE)
     elif args.config == "small":
         w = Dense(dg, [(128, 256, 512)])
+    elif args.config == "outlier":
+        w = Dense(dg, [(8192, 8192, 8192)], outlier=True)
     elif args.config == "decode":
         w = Decode(dg)
     else:

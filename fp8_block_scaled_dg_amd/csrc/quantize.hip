@@ -28,22 +28,35 @@ __device__ __forceinline__ float quotient_rn(float x, float s, float r) {
   return __builtin_fmaf(e, r, q);
 }
 
-// The quotient is formed on |x| (s > 0, so |x/s| = |x|/s) and the sign bit is
-// copied from x: the FMA correction would turn a -0 quotient into +0.
-__device__ __forceinline__ uint32_t encode1(float x, float s, float r, bool slow) {
+// |x| / s, correctly rounded, capped at 448.  The quotient is formed on |x|
+// (s > 0, so |x/s| = |x|/s) and the sign bit is restored by the caller: the
+// FMA correction would turn a -0 quotient into +0.  With a normal s the
+// quotient never exceeds 448 by more than a few ulps, which rounds to 448
+// anyway; with a subnormal s the scale itself may be off by a large factor
+// and the quotient can exceed 448, where E4M3 rounding saturates to 448.
+__device__ __forceinline__ float magnitude_quotient(float x, float s, float r, bool slow) {
   const float ax = fabsf(x);
   const float v = slow ? ax / s : quotient_rn(ax, s, r);
-  return e4m3_rne_mag(v) | ((__float_as_uint(x) >> 24) & 0x80u);
+  return fminf(v, 448.0f);
 }
 
-__device__ __forceinline__ uint32_t encode4(float4 v, float s, float r, bool slow) {
-  return encode1(v.x, s, r, slow) | (encode1(v.y, s, r, slow) << 8) |
-         (encode1(v.z, s, r, slow) << 16) | (encode1(v.w, s, r, slow) << 24);
-}
-
+// Sign bits of four values placed at bit 7 of each code byte.
 __device__ __forceinline__ uint32_t zero_codes4(float4 v) {
   return ((__float_as_uint(v.x) >> 31) << 7) | ((__float_as_uint(v.y) >> 31) << 15) |
          ((__float_as_uint(v.z) >> 31) << 23) | ((__float_as_uint(v.w) >> 31) << 31);
+}
+
+// Round to the nearest E4M3 code, ties to even, with v_cvt_pk_fp8_f32 (OCP
+// E4M3 on gfx950, default round-to-nearest-even mode).  Its result was
+// compared on an MI355X with a ties-to-even encoder written from the E4M3
+// field layout, for every binary32 magnitude below 464 and both signs
+// (including binary32 subnormals and -0): no difference.
+__device__ __forceinline__ uint32_t encode4(float4 v, float s, float r, bool slow) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(magnitude_quotient(v.x, s, r, slow),
+                                          magnitude_quotient(v.y, s, r, slow), 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(magnitude_quotient(v.z, s, r, slow),
+                                      magnitude_quotient(v.w, s, r, slow), p, true);
+  return (uint32_t)p | zero_codes4(v);
 }
 
 __device__ __forceinline__ float abs_max4(float m, float4 v) {

@@ -70,6 +70,8 @@ def _load():
     lib.orc_e4m3_decode_n.argtypes = [u8p, f64p, i64]
     lib.orc_quantize_block.restype = ctypes.c_int
     lib.orc_quantize_block.argtypes = [f32p, i64, i64, ctypes.c_int, u8p, f32p]
+    lib.orc_quantize_global.restype = ctypes.c_int
+    lib.orc_quantize_global.argtypes = [f32p, i64, i64, u8p, f32p]
     lib.orc_gemm_nt.restype = ctypes.c_int
     lib.orc_gemm_nt.argtypes = [u8p, f32p, ctypes.c_int, u8p, f32p, i64, i64, i64, f64p]
     lib.orc_gemm_nt_points.restype = ctypes.c_int
@@ -133,6 +135,22 @@ def quantize(x, block_rows: int = 128):
     if rc != 0:
         raise ValueError("oracle quantize rejected its input")
     return q, s
+
+
+def quantize_global(x):
+    """x: float32 [rows, cols] -> (q uint8 [rows, cols], scale float) with one
+    scale for the whole tensor (bjdmk.com.cn DeepGEMM page s3.3 contrasts this
+    with per-block scales)."""
+    x = _c(x, np.float32)
+    assert x.ndim == 2
+    rows, cols = x.shape
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty(1, dtype=np.float32)
+    rc = _load().orc_quantize_global(_ptr(x, ctypes.c_float), rows, cols,
+                                     _ptr(q, ctypes.c_uint8), _ptr(s, ctypes.c_float))
+    if rc != 0:
+        raise ValueError("oracle quantize_global rejected its input")
+    return q, float(s[0])
 
 
 def _check_gemm(qa, sa, a_block_rows, qb, sb):

@@ -179,6 +179,37 @@ int orc_quantize_block(const float *x, int64_t rows, int64_t cols, int block_row
     return 0;
 }
 
+/* Per-tensor ("global") scaling: the alternative that the block-wise method
+ * is contrasted with on the bjdmk.com.cn DeepGEMM page (s3.3: one scaling
+ * factor for the whole matrix instead of one per block).  The same steps as
+ * the block quantiser with a single block covering the tensor: amax over all
+ * elements, s = amax / 448 in binary32, v = x / s in binary32, E4M3 RNE. */
+int orc_quantize_global(const float *x, int64_t rows, int64_t cols, uint8_t *q, float *scale)
+{
+    int64_t i, n;
+    float amax = 0.0f, s;
+    if (!x || !q || !scale || rows < 0 || cols < 0)
+        return -1;
+    n = rows * cols;
+    for (i = 0; i < n; ++i) {
+        float a;
+        if (!isfinite(x[i]))
+            return -1;
+        a = fabsf(x[i]);
+        if (a > amax)
+            amax = a;
+    }
+    s = amax / 448.0f;
+    *scale = s;
+    for (i = 0; i < n; ++i) {
+        if (s == 0.0f)
+            q[i] = signbit(x[i]) ? 0x80 : 0x00;
+        else
+            q[i] = orc_e4m3_encode_arith(x[i] / s);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Dequantised NT GEMM ("... s2.2", "... s3.2"; NT layout from "DeepGEMM:   */
 /* GPU high-efficiency BLAS kernel library", s3.1 and s4.1).                 */

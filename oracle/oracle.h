@@ -56,6 +56,11 @@ void orc_e4m3_decode_n(const uint8_t *codes, double *out, int64_t n);
 int orc_quantize_block(const float *x, int64_t rows, int64_t cols, int block_rows,
                        uint8_t *q, float *scales);
 
+/* Per-tensor scaling (the baseline the block method is compared with): one
+ * FP32 scale = amax(x) / 448 for the whole tensor, then the same division and
+ * rounding.  Returns 0, or -1 on a bad argument / non-finite input. */
+int orc_quantize_global(const float *x, int64_t rows, int64_t cols, uint8_t *q, float *scale);
+
 /* Dequantised NT GEMM in FP64:
  * ref[m][n] = sum_kb (sa(m,kb) * sb(n,kb)) * sum_{k in kb} dec(qa[m][k]) dec(qb[n][k]).
  * qa [M][K], qb [N][K]; sa [ceil(K/128)][ceil(M/a_block_rows)];

@@ -83,6 +83,35 @@ def test_two_step_rounding_vectors_on_gpu(dg, orc):
     check(dg, orc, x, 1, "r3")
 
 
+@pytest.mark.parametrize("amax", [448.0, 56.0, 448.0 * 2.0 ** -70])
+def test_quantize_every_midpoint_and_its_neighbours(dg, orc, amax):
+    """Every block holds its amax (so s = amax/448 is a power of two and x/s
+    is exact) and then quotients at every E4M3 rounding midpoint -- between
+    consecutive magnitudes, subnormal range and the midpoint below the
+    smallest subnormal included -- and at the binary32 neighbours on both
+    sides, with both signs: the encoder's ties-to-even and its binade edges
+    are checked on every code boundary."""
+    mags = np.array(sorted({float(v) for v in orc.e4m3_decode(np.arange(0x7F, dtype=np.uint8))}))
+    mids = (mags[:-1] + mags[1:]) / 2.0
+    s = np.float32(amax) / np.float32(448.0)
+    vals = []
+    for m in mids.astype(np.float32):
+        for v in (np.nextafter(m, np.float32(0)), m, np.nextafter(m, np.float32(np.inf))):
+            vals += [v, -v]
+    unscaled = np.array(vals, np.float32)
+    vals = unscaled * s                   # exact: s is a power of two, no underflow
+    assert np.array_equal(vals / s, unscaled)
+    per_row = 127
+    rows = -(-len(vals) // per_row)
+    x = np.zeros((rows, 128), np.float32)
+    x[:, 0] = np.float32(amax)
+    flat = np.zeros(rows * per_row, np.float32)
+    flat[:len(vals)] = vals
+    x[:, 1:] = flat.reshape(rows, per_row)
+    for br in (1, 128):
+        check(dg, orc, x, br, "midpoints amax=%g br=%d" % (amax, br))
+
+
 @pytest.mark.parametrize("what,rows,cols,br", [
     ("C2a A", 4096, 2048, 128), ("C2c B", 8192, 8192, 128), ("C3 A M=64", 64, 16384, 1),
     ("C4 down A", 2816, 11008, 1)])

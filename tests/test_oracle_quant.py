@@ -124,3 +124,56 @@ def test_clipped_edge_blocks_equal_zero_padding(orc):
         qp, sp = orc.quantize(xp, br)
         assert np.array_equal(qp[:200, :333], q)
         assert np.array_equal(sp[:, :s.shape[1]], s)
+
+
+def test_global_scale_equals_single_block_and_bruteforce(orc):
+    """Per-tensor scaling (bjdmk.com.cn page s3.3 contrasts it with per-block
+    scales): for a tensor that is one 128x128 block it is the block quantiser;
+    for a larger tensor it is the same rounding with s = amax(tensor)/448,
+    checked element by element against the exact-rational nearest-even search."""
+    x = datagen.normal((100, 128), 1.0, seed=21, stream=1)
+    qg, sg = orc.quantize_global(x)
+    qb, sb = orc.quantize(x, 128)
+    assert sb.shape == (1, 1) and np.float32(sg).view(np.uint32) == sb[0, 0].view(np.uint32)
+    assert np.array_equal(qg, qb)
+
+    y = datagen.normal((5, 300), 1.0, seed=22, stream=1)
+    y[2, 7] = np.float32(37.5)          # one large element sets the tensor scale
+    y[0, 0] = -0.0
+    qg, sg = orc.quantize_global(y)
+    amax = max(abs(float(v)) for v in y.ravel())
+    assert np.float32(sg) == np.float32(amax) / np.float32(448.0)
+    for (i, j), v in np.ndenumerate(y):
+        want = exact.nearest_even_code(exact.Fraction(float(np.float32(v) / np.float32(sg))),
+                                       bool(np.signbit(v)))
+        assert qg[i, j] == want, (i, j)
+    assert qg[2, 7] == 0x7E             # the amax element lands on 448
+
+
+def test_global_scale_power_of_two_invariance_and_zero(orc):
+    x = datagen.normal((7, 260), 3.0, seed=23, stream=1)
+    q1, s1 = orc.quantize_global(x)
+    q2, s2 = orc.quantize_global(x * np.float32(2.0 ** -12))
+    assert np.array_equal(q1, q2) and s2 == s1 * 2.0 ** -12
+    z = np.zeros((3, 16), np.float32)
+    z[1, 2] = -0.0
+    qz, sz = orc.quantize_global(z)
+    assert sz == 0.0 and qz[1, 2] == 0x80 and int(qz.sum()) == 0x80
+
+
+def test_block_scaling_beats_global_on_outlier_activations(orc):
+    """The point of fine-grained scales: with heavy-tailed rows and a few
+    outlier channels, one tensor-wide scale is set by the largest element of
+    the whole tensor and pushes the other rows' values down to the coarse
+    (subnormal) end of E4M3; per-row 128-wide blocks adapt to each row.
+    Relative Frobenius error of the dequantised tensor (seeded input)."""
+    x, hot = datagen.student_t_outliers(64, 1024, seed=0, stream=5)
+    qb, sb = orc.quantize(x, 1)
+    qg, sg = orc.quantize_global(x)
+    dec = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    xb = dec[qb] * np.repeat(sb.T, 128, axis=1)[:, :1024]
+    xg = dec[qg] * sg
+    err_b = np.linalg.norm(xb - x) / np.linalg.norm(x)
+    err_g = np.linalg.norm(xg - x) / np.linalg.norm(x)
+    assert len(hot) == 10
+    assert err_b < 0.5 * err_g
