@@ -233,10 +233,13 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     for (int f = 0; f < 2; ++f) {
       const int n = n0 + wave * 32 + 16 * f + 4 * (lane >> 4);
       if (n < p.N) {
-        float* d = mine + (int64_t)m * p.N + n;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          __hip_atomic_store(d + r, acc[f][i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t* d = reinterpret_cast<uint64_t*>(mine + (int64_t)m * p.N + n);
+        const uint64_t lo = (uint64_t)__float_as_uint(acc[f][i][0]) |
+                            ((uint64_t)__float_as_uint(acc[f][i][1]) << 32);
+        const uint64_t hi = (uint64_t)__float_as_uint(acc[f][i][2]) |
+                            ((uint64_t)__float_as_uint(acc[f][i][3]) << 32);
+        __hip_atomic_store(d, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -250,37 +253,63 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   }
   __syncthreads();
   if (!s_last) return;
-  // the last split sums the S partials in split order (deterministic) -> BF16
+  // The last split sums the S partials in split order (deterministic) and
+  // writes BF16.  Thread t owns the float4 positions t + 256 j of the
+  // M x 128 tile; the loads of G splits x PJ positions are issued together so
+  // that one memory latency covers them, then added in split order.
+  constexpr int PJ = MP * (BN / 4) / 256;          // positions per thread: 2, 4 or 8
+  constexpr int G = 16 / PJ;                        // splits loaded per round
   const int ncols = min(BN, p.N - n0);
-  for (int idx = threadIdx.x; idx < p.M * (BN / 4); idx += 256) {
+  float4 sum[PJ];
+  bool live[PJ];
+  int64_t off[PJ];
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    const int idx = threadIdx.x + 256 * j;
     const int m = idx / (BN / 4);
     const int cc = (idx - m * (BN / 4)) * 4;
-    if (cc >= ncols) continue;
-    const int64_t o = (int64_t)m * p.N + n0 + cc;
-    // load every split's partial first (independent device-scope loads in
-    // flight together), then add them in split order
-    float4 part[kMaxSplits];
+    live[j] = m < p.M && cc < ncols;
+    off[j] = (int64_t)m * p.N + n0 + cc;
+    sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int s0 = 0; s0 < p.S; s0 += G) {
+    uint64_t part[G][PJ][2];
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
-      if (sp < p.S) {
-        const float* src = p.partials + (int64_t)sp * p.M * p.N + o;
-        part[sp].x = __hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        part[sp].y = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        part[sp].z = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        part[sp].w = __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    float t[4] = {part[0].x, part[0].y, part[0].z, part[0].w};
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int sp = 1; sp < kMaxSplits; ++sp) {
-      if (sp < p.S) {
-        t[0] += part[sp].x; t[1] += part[sp].y; t[2] += part[sp].z; t[3] += part[sp].w;
+      for (int j = 0; j < PJ; ++j) {
+        const int sp = s0 + g;
+        if (sp < p.S && live[j]) {
+          const uint64_t* src =
+              reinterpret_cast<const uint64_t*>(p.partials + (int64_t)sp * p.M * p.N + off[j]);
+          part[g][j][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          part[g][j][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
-    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < PJ; ++j) {
+        if (s0 + g < p.S && live[j]) {
+          const float4 v = make_float4(__uint_as_float((uint32_t)part[g][j][0]),
+                                       __uint_as_float((uint32_t)(part[g][j][0] >> 32)),
+                                       __uint_as_float((uint32_t)part[g][j][1]),
+                                       __uint_as_float((uint32_t)(part[g][j][1] >> 32)));
+          if (s0 + g == 0) {
+            sum[j] = v;
+          } else {
+            sum[j].x += v.x; sum[j].y += v.y; sum[j].z += v.z; sum[j].w += v.w;
+          }
+        }
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    if (!live[j]) continue;
     uint2 v;
-    v.x = bf16_rne(t[0]) | (bf16_rne(t[1]) << 16);
-    v.y = bf16_rne(t[2]) | (bf16_rne(t[3]) << 16);
-    *reinterpret_cast<uint2*>(p.c + o) = v;
+    v.x = bf16_rne(sum[j].x) | (bf16_rne(sum[j].y) << 16);
+    v.y = bf16_rne(sum[j].z) | (bf16_rne(sum[j].w) << 16);
+    *reinterpret_cast<uint2*>(p.c + off[j]) = v;
   }
   if (threadIdx.x == 0)  // leave the counter zeroed for the next call
     __hip_atomic_store(&g_splitk_counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -304,13 +333,14 @@ int choose_splits(int64_t M, int64_t N, int64_t K) {
     return (int)(f > kMaxSplits ? kMaxSplits : f);
   }
   // ~one workgroup per CU; more splits only add partial traffic, which grows
-  // with M (measured best: 1 split at N = 24576, 4 at N = 4096 and 7168)
-  int64_t S = 256 / tiles;
+  // with M.  Measured on MI355X: M = 64 wants 1 split at N = 24576 and 4 at
+  // N = 4096 and 7168; M <= 16 gains from ~two workgroups per CU (8 splits)
+  // when N gives few tiles, and loses when it gives many (N = 24576).
+  int64_t S = (M <= 16 && tiles < 128) ? 512 / tiles : 256 / tiles;
   S = S < 1 ? 1 : S;
-  S = S > 4 ? 4 : S;
+  S = S > (M <= 16 ? 8 : 4) ? (M <= 16 ? 8 : 4) : S;
   S = S > nkb / 3 ? nkb / 3 : S;                // keep >= 3 K blocks (one ring round) per split
   S = S < 1 ? 1 : S;
-  (void)M;
   return (int)S;
 }
 

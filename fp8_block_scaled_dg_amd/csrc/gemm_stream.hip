@@ -227,18 +227,19 @@ hipError_t launch_ks(const StreamArgs& p, hipStream_t stream) {
 
 }  // namespace
 
-// Measured on MI355X (kernel trace): for M <= 16 the streaming kernel wins
-// unless N alone supplies enough 128-row LDS-ring workgroups (N >= 16384);
-// for larger M the ring kernel (A staged once per workgroup) wins.  An
-// override DG_DECODE_KERNEL=ring|stream is read once, for tuning sweeps.
+// Measured on MI355X: for M <= 8 the streaming kernel wins unless N alone
+// supplies enough 128-row LDS-ring workgroups (N >= 16384).  At M = 16 every
+// streaming wave re-reads as many bytes of A as of B, so the ring kernel (A
+// staged once per workgroup, split-K) wins once B is large (7168 x 16384),
+// while the streaming kernel keeps small B (4096 x 4096).  An override
+// DG_DECODE_KERNEL=ring|stream is read once, for tuning sweeps.
 bool stream_preferred(int64_t M, int64_t N, int64_t K) {
   static const int forced = [] {
     const char* e = getenv("DG_DECODE_KERNEL");
     return e ? (e[0] == 's' ? 1 : (e[0] == 'r' ? 2 : 0)) : 0;
   }();
   if (forced) return forced == 1;
-  (void)K;
-  return M <= 16 && N < 16384;
+  return N < 16384 && (M <= 8 || (M <= 16 && N * K <= (int64_t(32) << 20)));
 }
 
 hipError_t launch_gemm_stream(const GemmProblem& q, hipStream_t stream) {

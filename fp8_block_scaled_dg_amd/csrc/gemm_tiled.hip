@@ -31,8 +31,8 @@
 //    permutation is applied to the global source addresses), so every 8
 //    consecutive lanes still fetch one full 128-byte row segment.
 //  * Workgroup ids are remapped so that each XCD (ids round-robin over 8
-//    XCDs) works on a contiguous, M-grouped patch of tiles that shares A and
-//    B panels in its own L2.
+//    XCDs) works on a contiguous patch of tiles that shares A and B panels in
+//    its own L2 (see map_tile).
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
@@ -122,15 +122,28 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
   return r;
 }
 
-__device__ __forceinline__ void map_tile(const TiledArgs& p, int& tm, int& tn) {
-  int bid = blockIdx.x;
+// Workgroup ids are dealt round-robin to the 8 XCDs (id % 8), each with its
+// own L2.  The id is first turned into a position L in a tile order such that
+// every XCD gets a contiguous run of L (a bijection for any tile count), then
+// L is mapped to a tile.  Dense: groups of group_m tile-rows swept along N,
+// so concurrently running tiles share A and B panels.  Grouped: N-tile-major,
+// so the tiles that read one expert's B tile (all its row blocks) run back to
+// back on the same XCD and the B tile comes from HBM once.
+__device__ __forceinline__ void map_tile(const TiledArgs& p, bool grouped, int& tm, int& tn) {
+  const int bid = blockIdx.x;
   const int total = p.tiles_m * p.tiles_n;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+  const int x = bid & 7, per = total >> 3, extra = total & 7;
+  const int L = x * per + min(x, extra) + (bid >> 3);
+  if (grouped) {
+    tn = L / p.tiles_m;
+    tm = L - tn * p.tiles_m;
+    return;
+  }
   const int per_group = p.group_m * p.tiles_n;
-  const int group = bid / per_group;
+  const int group = L / per_group;
   const int first_m = group * p.group_m;
   const int gsz = min(p.tiles_m - first_m, p.group_m);
-  const int rem = bid - group * per_group;
+  const int rem = L - group * per_group;
   tm = first_m + rem % gsz;
   tn = rem / gsz;
 }
@@ -194,7 +207,7 @@ gemm_tiled_kernel(TiledArgs p) {
   const int wn = wave / WM;
 
   int tm, tn;
-  map_tile(p, tm, tn);
+  map_tile(p, GROUPED, tm, tn);
   const int n0 = tn * BN;
   int m0 = tm * BM;
   int rows_end = p.M;  // rows [m0, rows_end) are stored
@@ -371,7 +384,7 @@ gemm_ring_kernel(TiledArgs p) {
   const int wn = wave / WM;
 
   int tm, tn;
-  map_tile(p, tm, tn);
+  map_tile(p, GROUPED, tm, tn);
   const int n0 = tn * BN;
   int m0 = tm * BM;
   int rows_end = p.M;
