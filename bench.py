@@ -22,7 +22,9 @@ hold them), --config moe (8 experts, 1024 tokens top-2, up and down
 projections), --config small (128x256x512), --config outlier (8192^3 with
 heavy-tailed, hot-channel activations and 1x128 activation scales),
 --config copy (a plain device copy of known size, used to calibrate the
-FETCH_SIZE/WRITE_SIZE counters).
+FETCH_SIZE/WRITE_SIZE counters), --config peak (the FP8 MFMA-loop probe: the
+matrix-core rate and shader clock this GPU sustains; the dense line also
+carries it as roofline.measured_peak).
 
 Prints ONE JSON line on stdout.
 """
@@ -396,6 +398,49 @@ class Moe:
         return None
 
 
+def measured_mfma_peak(blocks=1024, iters=10000, reps=3):
+    """Dense FP8 matrix-core rate this GPU sustains on a pure MFMA loop
+    (4 waves per SIMD, 8 independent 16x16x128 chains per wave, pseudo-random
+    E4M3 operands), and the shader clock it ran at (s_memtime cycles over the
+    100 MHz s_memrealtime interval of one wave).  None without the probe."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_block_scaled_dg_amd", "lib", "libdg_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.dgp_mfma_fp8_loop.restype = ctypes.c_int
+    lib.dgp_mfma_fp8_loop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.dgp_mfma_fp8_loop(out.data_ptr(), clk.data_ptr(), blocks, iters,
+                                   ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("MFMA probe launch failed (%d)" % rc)
+
+    launch()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        launch()
+        e.record(stream)
+        e.synchronize()
+        ms = s.elapsed_time(e)
+        best = ms if best is None else min(best, ms)
+    cycles, ticks = (int(v) for v in clk.cpu().tolist())
+    flop = float(blocks) * 4 * iters * 8 * 65536
+    return {"tflops": flop / (best * 1e-3) / 1e12,
+            "sclk_ghz": cycles / (ticks / 100e6) / 1e9 if ticks > 0 else None,
+            "what": "FP8 16x16x128 MFMA loop, %d workgroups x 4 waves, %d x 8 MFMAs per wave, "
+                    "best of %d" % (blocks, iters, reps)}
+
+
 def run_copy(args):
     """A plain device-to-device copy of known size (for counter calibration)."""
     n = 1 << 30
@@ -423,7 +468,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="dense",
-                    choices=["dense", "decode", "moe", "small", "outlier", "copy"])
+                    choices=["dense", "decode", "moe", "small", "outlier", "copy", "peak"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -438,6 +483,13 @@ def main():
     torch.cuda.set_device(0)
     if args.config == "copy":
         run_copy(args)
+        return
+    if args.config == "peak":
+        mp = measured_mfma_peak()
+        print(json.dumps({"metric": "measured FP8 MFMA peak", "value": mp and mp["tflops"],
+                          "unit": "TFLOP/s", "published_peak": PEAK_FP8_TFLOPS,
+                          "sclk_ghz": mp and mp["sclk_ghz"], "what": mp and mp["what"],
+                          "n_gpus": 1}), flush=True)
         return
 
     import fp8_block_scaled_dg_amd as dg
@@ -494,6 +546,13 @@ def main():
 
     breakdown = w.breakdown(timer, args.kernel_reps)
     roof = w.roofline(timer, args.kernel_reps)
+    if roof["bound"] == "mfma":
+        mp = measured_mfma_peak()
+        if mp is not None:
+            roof["measured_peak"] = mp["tflops"]
+            roof["frac_of_measured_peak"] = roof["achieved"] / mp["tflops"]
+            roof["measured_peak_sclk_ghz"] = mp["sclk_ghz"]
+            roof["measured_peak_what"] = mp["what"]
     log("roofline", roof)
     cpu = None
     if not args.no_cpu_baseline:
