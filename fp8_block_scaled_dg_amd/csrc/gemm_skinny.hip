@@ -8,9 +8,9 @@
 // scales/operands rather than arithmetic dominates.
 //
 // gfx950 mapping
-//  * A workgroup (4 waves) owns 128 rows of B (one 128-row scale block) and a
-//    contiguous range of K blocks.  B streams through a 3-stage LDS ring fed by
-//    global_load_lds_dwordx4 (16 KB of B per stage, 8 consecutive lanes per
+//  * A workgroup (4 waves) owns 128 (or 64) rows of B inside one 128-row scale
+//    block and a contiguous range of K blocks.  B streams through a 3-stage
+//    LDS ring fed by global_load_lds_dwordx4 (16 KB of B per stage, 8 consecutive lanes per
 //    128-byte row, chunk permutation as in the tiled kernel); a workgroup
 //    needs <= 75 KB of LDS, so two run per CU with 4 stages (64 KB) of B in
 //    flight between them.  A (M padded to 16/32/64 rows, rows past M clamped)
@@ -19,7 +19,7 @@
 //    is unrolled by the ring depth, so the compiler's LDS-DMA dependency
 //    tracking can see that the slot being filled is not the slot being read
 //    (with one array it waits for every outstanding load before each read).
-//  * Each wave computes 32 rows of B x MP columns of A with
+//  * Each wave computes 32 (or 16) rows of B x MP columns of A with
 //    v_mfma_f32_16x16x128_f8f6f4 (B rows drive the instruction's first
 //    operand), promoting each 128-K partial with sa*sb in FP32.
 //  * Split-K when N/128 workgroups cannot fill the GPU: split s writes its
@@ -40,7 +40,7 @@ namespace {
 constexpr int BN = 128;
 constexpr int BK = 128;
 constexpr int NS = 3;              // LDS ring depth (<= 75 KB: two workgroups per CU)
-constexpr int kMaxCounters = 8192; // N up to 1M with BN = 128
+constexpr int kMaxCounters = 8192; // tiles: N up to 1M with 128-row tiles
 constexpr int kMaxSplits = 16;
 
 __device__ int g_splitk_counters[kMaxCounters];
@@ -71,10 +71,11 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
   return r;
 }
 
-template <int MP>
+template <int MP, int F>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
+  constexpr int BNT = 64 * F;                     // B rows per workgroup (F fragments per wave)
   constexpr int MPE = MP < 32 ? 32 : MP;          // A rows staged (>= 4 DMA instructions)
-  constexpr int B_BYTES = BN * BK;                // 16 KB
+  constexpr int B_BYTES = BNT * BK;               // 8 or 16 KB
   constexpr int A_BYTES = MPE * BK;
   constexpr int SA_BYTES = 4 * 256;               // one 64-float copy per wave
   constexpr int SB_BYTES = 4 * 256;               // B block scale (64 copies) per wave
@@ -93,7 +94,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   const int wave = threadIdx.x >> 6;
   const int nt = blockIdx.x / p.S;
   const int split = blockIdx.x - nt * p.S;
-  const int n0 = nt * BN;
+  const int n0 = nt * BNT;
   const int kb0 = (int)((int64_t)split * p.nkb / p.S);
   const int kb1 = (int)((int64_t)(split + 1) * p.nkb / p.S);
   const int nk = kb1 - kb0;  // >= 1 (S <= nkb)
@@ -142,9 +143,9 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   const int off0 = fr * 128 + (((2 * (lane >> 4)) ^ lds_swz(fr)) * 16);
   const int off1 = fr * 128 + (((2 * (lane >> 4) + 1) ^ lds_swz(fr)) * 16);
 
-  v4f acc[2][NI];
+  v4f acc[F][NI];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < F; ++f)
 #pragma unroll
     for (int i = 0; i < NI; ++i) acc[f][i] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -181,8 +182,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) af[i] = read_frag(cur + B_BYTES, 16 * i, off0, off1);
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const v8i bf = read_frag(cur, wave * 32 + 16 * f, off0, off1);
+    for (int f = 0; f < F; ++f) {
+      const v8i bf = read_frag(cur, wave * 16 * F + 16 * f, off0, off1);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const v4f part =
@@ -200,15 +201,15 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   // drain the re-staged loads past the range before the workgroup exits
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 
-  // lane owns C[m = 16i + l%16][n = n0 + 32*wave + 16f + 4*(l/16) + r]
+  // lane owns C[m = 16i + l%16][n = n0 + 16*F*wave + 16f + 4*(l/16) + r]
   if (p.S == 1) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int m = 16 * i + fr;
       if (m >= p.M) continue;
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int n = n0 + wave * 32 + 16 * f + 4 * (lane >> 4);
+      for (int f = 0; f < F; ++f) {
+        const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
         if (n < p.N) {
           uint2 v;
           v.x = bf16_rne(acc[f][i][0]) | (bf16_rne(acc[f][i][1]) << 16);
@@ -230,8 +231,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     const int m = 16 * i + fr;
     if (m >= p.M) continue;
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int n = n0 + wave * 32 + 16 * f + 4 * (lane >> 4);
+    for (int f = 0; f < F; ++f) {
+      const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
       if (n < p.N) {
         uint64_t* d = reinterpret_cast<uint64_t*>(mine + (int64_t)m * p.N + n);
         const uint64_t lo = (uint64_t)__float_as_uint(acc[f][i][0]) |
@@ -257,17 +258,17 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   // writes BF16.  Thread t owns the float4 positions t + 256 j of the
   // M x 128 tile; the loads of G splits x PJ positions are issued together so
   // that one memory latency covers them, then added in split order.
-  constexpr int PJ = MP * (BN / 4) / 256;          // positions per thread: 2, 4 or 8
+  constexpr int PJ = MP * (BNT / 4) / 256;         // positions per thread: 1 .. 8
   constexpr int G = 16 / PJ;                        // splits loaded per round
-  const int ncols = min(BN, p.N - n0);
+  const int ncols = min(BNT, p.N - n0);
   float4 sum[PJ];
   bool live[PJ];
   int64_t off[PJ];
 #pragma unroll
   for (int j = 0; j < PJ; ++j) {
     const int idx = threadIdx.x + 256 * j;
-    const int m = idx / (BN / 4);
-    const int cc = (idx - m * (BN / 4)) * 4;
+    const int m = idx / (BNT / 4);
+    const int cc = (idx - m * (BNT / 4)) * 4;
     live[j] = m < p.M && cc < ncols;
     off[j] = (int64_t)m * p.N + n0 + cc;
     sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -324,8 +325,26 @@ int forced_splits() {
   return v;
 }
 
+// B rows per workgroup: 128, or 64 when M > 16 and N gives fewer than 128
+// tiles of 128 rows.  64-row tiles re-read A twice as often, but reach a full
+// GPU with fewer K splits (less partial traffic, shorter reductions):
+// measured on MI355X at M = 64, N = 7168, K = 16384: 39 us (64 rows, 2
+// splits) vs 45 us (128 rows, 4 splits); N = 4096, K = 4096: 11.7 vs 18.7 us.
+// DG_SKINNY_BN=64|128 overrides it (read once, for tuning sweeps).
+int choose_bn(int64_t M, int64_t N) {
+  static const int forced = [] {
+    const char* e = getenv("DG_SKINNY_BN");
+    return e ? atoi(e) : 0;
+  }();
+  const bool fits64 = (N + 63) / 64 <= kMaxCounters;
+  if (forced == 64 && fits64) return 64;
+  if (forced == 128) return 128;
+  return (M > 16 && (N + 127) / 128 < 128 && fits64) ? 64 : 128;
+}
+
 int choose_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = (N + BN - 1) / BN;
+  const int bn = choose_bn(M, N);
+  const int64_t tiles = (N + bn - 1) / bn;
   const int64_t nkb = K / BK;
   if (forced_splits() > 0) {
     int64_t f = forced_splits();
@@ -333,9 +352,10 @@ int choose_splits(int64_t M, int64_t N, int64_t K) {
     return (int)(f > kMaxSplits ? kMaxSplits : f);
   }
   // ~one workgroup per CU; more splits only add partial traffic, which grows
-  // with M.  Measured on MI355X: M = 64 wants 1 split at N = 24576 and 4 at
-  // N = 4096 and 7168; M <= 16 gains from ~two workgroups per CU (8 splits)
-  // when N gives few tiles, and loses when it gives many (N = 24576).
+  // with M.  Measured on MI355X: M = 64 wants 1 split at N = 24576 (128-row
+  // tiles), 2 at N = 7168 and 4 at N = 4096 (64-row tiles); M <= 16 gains
+  // from ~two workgroups per CU (8 splits) when N gives few tiles, and loses
+  // when it gives many (N = 24576).
   int64_t S = (M <= 16 && tiles < 128) ? 512 / tiles : 256 / tiles;
   S = S < 1 ? 1 : S;
   S = S > (M <= 16 ? 8 : 4) ? (M <= 16 ? 8 : 4) : S;
@@ -368,13 +388,23 @@ hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t work
   if (workspace == nullptr || workspace_bytes < skinny_workspace_bytes(q.M, q.N, q.K)) S = 1;
   p.S = S;
   p.partials = static_cast<float*>(workspace);
-  const unsigned grid = (unsigned)(((q.N + BN - 1) / BN) * S);
-  if (q.M <= 16)
-    hipLaunchKernelGGL(gemm_skinny_kernel<16>, dim3(grid), dim3(256), 0, stream, p);
-  else if (q.M <= 32)
-    hipLaunchKernelGGL(gemm_skinny_kernel<32>, dim3(grid), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(gemm_skinny_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+  const int bn = choose_bn(q.M, q.N);
+  const unsigned grid = (unsigned)(((q.N + bn - 1) / bn) * S);
+  if (bn == 64) {
+    if (q.M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 1>), dim3(grid), dim3(256), 0, stream, p);
+    else if (q.M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 1>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 1>), dim3(grid), dim3(256), 0, stream, p);
+  } else {
+    if (q.M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 2>), dim3(grid), dim3(256), 0, stream, p);
+    else if (q.M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 2>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 2>), dim3(grid), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
