@@ -100,6 +100,14 @@ def test_grouped_validation(dg):
     assert gg(lib, mi=ctypes.c_void_p(0x10002)) == 4
 
 
+def test_small_m_workspace_too_small_is_rejected(dg):
+    lib = dg.lib
+    need = dg.dg_fp8_gemm_nt_workspace_bytes(16, 4096, 4096)
+    assert need > 16                      # this shape plans a split-K reduction
+    assert g(lib, M=16, N=4096, K=4096, ws=P, wsb=16) == 5
+    assert g(lib, M=16, N=4096, K=4096, ws=P1, wsb=need) == 4   # misaligned workspace
+
+
 def test_workspace_query_is_host_only(dg):
     assert dg.dg_fp8_gemm_nt_workspace_bytes(1, 4096, 4096) >= 0
     assert dg.dg_fp8_gemm_nt_workspace_bytes(0, 4096, 4096) == 0
