@@ -237,3 +237,83 @@ def test_outlier_activations_block_vs_global_full_size(dg, orc):
           "rms", rms)
     # (on a 64x1024x8192 slice of this input the oracle gives 2.8% vs 3.6%)
     assert errs["block"] < errs["per-tensor"]
+
+
+@pytest.mark.parametrize("M,N,K,br", [(64, 4096, 4096, 1), (16, 7168, 2048, 1), (1, 4096, 1024, 1),
+                                      (256, 512, 1024, 128)])
+def test_graph_replays_match_eager(dg, orc, M, N, K, br):
+    """The split-K plans keep state in a device counter array that each call
+    must leave zeroed; a HIP graph of several GEMMs, replayed repeatedly with
+    eager launches and synchronisations in between, must reproduce the eager
+    output bit for bit on every replay."""
+    qa, sa, qb, sb = operands(orc, M, N, K, br, seed=K + M)
+    a, b, sa_d, sb_d = dev(qa), dev(qb), dev(sa), dev(sb)
+    wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    c_eager = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm_nt(c_eager, a, b, sa_d, sb_d, br, workspace=ws)
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(c_eager) for _ in range(3)]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for o in outs:
+                dg.dg_fp8_gemm_nt(o, a, b, sa_d, sb_d, br, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.equal(o.view(torch.int16), c_eager.view(torch.int16)), "replay %d" % rep
+        c2 = torch.empty_like(c_eager)           # eager work between replays
+        dg.dg_fp8_gemm_nt(c2, a, b, sa_d, sb_d, br, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(c2.view(torch.int16), c_eager.view(torch.int16))
+
+
+def test_gemm_at_32bit_offset_limit(dg, orc):
+    """Largest operands the ABI accepts: M*K and N*K just below 2^32 bytes
+    (byte offsets inside the kernels are 32-bit), ragged M and N.  Codes and
+    scales are drawn on the GPU; the oracle sees only the sampled rows."""
+    M, N, K = 32767, 32760, 131072
+    assert M * K < 2 ** 32 and N * K < 2 ** 32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+
+    def codes(R):
+        q = torch.randint(0, 0x7E, (R, K), dtype=torch.uint8, device="cuda", generator=g)
+        q |= torch.randint(0, 2, (R, K), dtype=torch.uint8, device="cuda", generator=g) << 7
+        return q
+    qa, qb = codes(M), codes(N)
+    sa = (torch.rand((K // 128, (M + 127) // 128), device="cuda", generator=g) + 0.5) * 1e-3
+    sb = (torch.rand((K // 128, (N + 127) // 128), device="cuda", generator=g) + 0.5) * 1e-3
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm_nt(c, qa, qb, sa, sb, 128)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 1, 255, 256, M // 2, M - 2, M - 1}), np.int64)
+    blocks = [0, 100, (N - 1) // 128]                       # the last block is ragged
+    cols = np.concatenate([np.arange(b * 128, min(N, b * 128 + 128)) for b in blocks])
+    qa_h = qa[torch.from_numpy(rows).cuda()].cpu().numpy()
+    qb_h = qb[torch.from_numpy(cols).cuda()].cpu().numpy()
+    sa_h = sa[:, torch.from_numpy(rows // 128).cuda()].cpu().numpy()        # one column per row
+    sb_h = sb[:, torch.tensor(blocks, device="cuda")].cpu().numpy()
+    # local problem: row i of qa_h has its own 128-row scale column (a_block_rows = 1 view)
+    pm = np.repeat(np.arange(rows.size), cols.size)
+    pn = np.tile(np.arange(cols.size), rows.size)
+    nb_local = np.repeat(np.arange(len(blocks)), [min(N, b * 128 + 128) - b * 128 for b in blocks])
+    # the oracle indexes sb by n // 128: lay the sampled B rows out block-aligned
+    qb_al = np.zeros((len(blocks) * 128, K), np.uint8)
+    pos = np.concatenate([np.arange(min(N, b * 128 + 128) - b * 128) + i * 128 for i, b in enumerate(blocks)])
+    qb_al[pos] = qb_h
+    ref = orc.gemm_nt_points(qa_h, np.ascontiguousarray(sa_h), qb_al, np.ascontiguousarray(sb_h),
+                             pm, pos[pn], a_block_rows=1)
+    assert np.array_equal(nb_local[pn], pos[pn] // 128)
+    got = c[torch.from_numpy(rows[pm]).cuda(), torch.from_numpy(cols[pn]).cuda()]
+    got = got.float().cpu().numpy().astype(np.float64)
+    assert_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="32-bit limit")
+    del qa, qb, c
+    torch.cuda.empty_cache()
