@@ -275,11 +275,9 @@ def test_graph_replays_match_eager(dg, orc, M, N, K, br):
         assert torch.equal(c2.view(torch.int16), c_eager.view(torch.int16))
 
 
-def test_gemm_at_32bit_offset_limit(dg, orc):
-    """Largest operands the ABI accepts: M*K and N*K just below 2^32 bytes
-    (byte offsets inside the kernels are 32-bit), ragged M and N.  Codes and
-    scales are drawn on the GPU; the oracle sees only the sampled rows."""
-    M, N, K = 32767, 32760, 131072
+def check_at_limit(dg, orc, M, N, K, br):
+    """Codes and scales are drawn on the GPU; the oracle sees only the sampled
+    rows of A and three 128-row blocks of B (the last one ragged)."""
     assert M * K < 2 ** 32 and N * K < 2 ** 32
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
@@ -289,31 +287,45 @@ def test_gemm_at_32bit_offset_limit(dg, orc):
         q |= torch.randint(0, 2, (R, K), dtype=torch.uint8, device="cuda", generator=g) << 7
         return q
     qa, qb = codes(M), codes(N)
-    sa = (torch.rand((K // 128, (M + 127) // 128), device="cuda", generator=g) + 0.5) * 1e-3
+    sa = (torch.rand((K // 128, (M + br - 1) // br), device="cuda", generator=g) + 0.5) * 1e-3
     sb = (torch.rand((K // 128, (N + 127) // 128), device="cuda", generator=g) + 0.5) * 1e-3
+    wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    dg.dg_fp8_gemm_nt(c, qa, qb, sa, sb, 128)
+    dg.dg_fp8_gemm_nt(c, qa, qb, sa, sb, br, workspace=ws)
     torch.cuda.synchronize()
-    rows = np.array(sorted({0, 1, 255, 256, M // 2, M - 2, M - 1}), np.int64)
-    blocks = [0, 100, (N - 1) // 128]                       # the last block is ragged
+    rows = np.array(sorted({0, min(1, M - 1), min(255, M - 1), min(256, M - 1), M // 2, max(M - 2, 0),
+                            M - 1}), np.int64)
+    assert rows.max() < M
+    blocks = [0, min(100, (N - 1) // 128), (N - 1) // 128]
+    blocks = sorted(set(blocks))
     cols = np.concatenate([np.arange(b * 128, min(N, b * 128 + 128)) for b in blocks])
     qa_h = qa[torch.from_numpy(rows).cuda()].cpu().numpy()
     qb_h = qb[torch.from_numpy(cols).cuda()].cpu().numpy()
-    sa_h = sa[:, torch.from_numpy(rows // 128).cuda()].cpu().numpy()        # one column per row
+    sa_h = sa[:, torch.from_numpy(rows // br).cuda()].cpu().numpy()         # one column per row
     sb_h = sb[:, torch.tensor(blocks, device="cuda")].cpu().numpy()
-    # local problem: row i of qa_h has its own 128-row scale column (a_block_rows = 1 view)
-    pm = np.repeat(np.arange(rows.size), cols.size)
-    pn = np.tile(np.arange(cols.size), rows.size)
-    nb_local = np.repeat(np.arange(len(blocks)), [min(N, b * 128 + 128) - b * 128 for b in blocks])
     # the oracle indexes sb by n // 128: lay the sampled B rows out block-aligned
     qb_al = np.zeros((len(blocks) * 128, K), np.uint8)
-    pos = np.concatenate([np.arange(min(N, b * 128 + 128) - b * 128) + i * 128 for i, b in enumerate(blocks)])
+    pos = np.concatenate([np.arange(min(N, b * 128 + 128) - b * 128) + i * 128
+                          for i, b in enumerate(blocks)])
     qb_al[pos] = qb_h
+    pm = np.repeat(np.arange(rows.size), cols.size)
+    pn = np.tile(np.arange(cols.size), rows.size)
     ref = orc.gemm_nt_points(qa_h, np.ascontiguousarray(sa_h), qb_al, np.ascontiguousarray(sb_h),
                              pm, pos[pn], a_block_rows=1)
-    assert np.array_equal(nb_local[pn], pos[pn] // 128)
     got = c[torch.from_numpy(rows[pm]).cuda(), torch.from_numpy(cols[pn]).cuda()]
     got = got.float().cpu().numpy().astype(np.float64)
-    assert_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="32-bit limit")
+    assert_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="limit %dx%dx%d" % (M, N, K))
     del qa, qb, c
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M,N,K,br", [
+    (32767, 32760, 131072, 128),   # tiled kernel
+    (1, 16376, 262144, 1),         # streaming small-M kernel
+    (16, 32760, 131072, 1),        # LDS-ring small-M kernel
+    (64, 32760, 131072, 1)])
+def test_gemm_at_32bit_offset_limit(dg, orc, M, N, K, br):
+    """Largest operands the ABI accepts: M*K and N*K just below 2^32 bytes
+    (byte offsets inside the kernels are 32-bit), ragged N."""
+    check_at_limit(dg, orc, M, N, K, br)
