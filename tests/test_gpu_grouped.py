@@ -120,3 +120,42 @@ def test_grouped_moe_full_size_sampled(dg, orc, proj, N, K):
             # rows of one expert: the dense oracle on that expert's weights
             ref[sel] = orc.gemm_nt_points(qa, sa, qb[e], sb[e], pm[sel], pn[sel], a_block_rows=1)
     assert_close(c[pm, pn], ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="moe " + proj)
+
+
+def test_grouped_at_32bit_offset_limit(dg, orc):
+    """Two experts whose N*K is just below 2^32 bytes each (the per-expert
+    base is 64-bit, offsets inside an expert 32-bit); rows: expert 0 with 200
+    routed rows (2 blocks, the second padded), expert 1 with 128 (1 block)."""
+    G, N, K = 2, 32760, 131072
+    mi = np.full(384, -1, np.int32)
+    mi[:200] = 0
+    mi[256:384] = 1
+    M = mi.shape[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    qa = torch.randint(0, 0x7E, (M, K), dtype=torch.uint8, device="cuda", generator=g)
+    qb = torch.randint(0, 0x7E, (G, N, K), dtype=torch.uint8, device="cuda", generator=g)
+    sa = (torch.rand((K // 128, M), device="cuda", generator=g) + 0.5) * 1e-3
+    sb = (torch.rand((G, K // 128, N // 128 + 1), device="cuda", generator=g) + 0.5) * 1e-3
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_grouped_gemm_contig(c, qa, qb, sa, sb, 1, dev(mi))
+    torch.cuda.synchronize()
+    assert torch.all(c[torch.from_numpy(np.nonzero(mi < 0)[0]).cuda()] == 0)
+    blocks = [0, (N - 1) // 128]
+    cols = np.concatenate([np.arange(b * 128, min(N, b * 128 + 128)) for b in blocks])
+    pos = np.concatenate([np.arange(min(N, b * 128 + 128) - b * 128) + i * 128
+                          for i, b in enumerate(blocks)])
+    for e, rows in ((0, np.array([0, 130, 199])), (1, np.array([256, 300, 383]))):
+        qa_h = qa[torch.from_numpy(rows).cuda()].cpu().numpy()
+        sa_h = np.ascontiguousarray(sa[:, torch.from_numpy(rows).cuda()].cpu().numpy())
+        qb_al = np.zeros((len(blocks) * 128, K), np.uint8)
+        qb_al[pos] = qb[e][torch.from_numpy(cols).cuda()].cpu().numpy()
+        sb_h = np.ascontiguousarray(sb[e][:, torch.tensor(blocks, device="cuda")].cpu().numpy())
+        pm = np.repeat(np.arange(rows.size), cols.size)
+        pn = np.tile(np.arange(cols.size), rows.size)
+        ref = orc.gemm_nt_points(qa_h, sa_h, qb_al, sb_h, pm, pos[pn], a_block_rows=1)
+        got = c[torch.from_numpy(rows[pm]).cuda(), torch.from_numpy(cols[pn]).cuda()]
+        assert_close(got.float().cpu().numpy().astype(np.float64), ref,
+                     rms=float(np.sqrt(np.mean(ref ** 2))), what="grouped limit e%d" % e)
+    del qa, qb, c
+    torch.cuda.empty_cache()
