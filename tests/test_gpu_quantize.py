@@ -131,3 +131,27 @@ def test_quantize_deterministic(dg):
     q1, s1 = dg.to_fp8(x, 128)
     q2, s2 = dg.to_fp8(x, 128)
     assert torch.equal(q1, q2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("rows,cols,br", [(65535 * 32, 128, 1), (65535 * 128, 16, 128)])
+def test_quantize_at_grid_limit(dg, orc, rows, cols, br):
+    """The largest row counts the quantiser's launch accepts (65535 workgroup
+    rows); one more block row is rejected on the host.  Sampled blocks (rows
+    are independent across blocks) are compared with the oracle bit for bit."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    x = torch.randn((rows, cols), device="cuda", generator=g)
+    q, s = dg.to_fp8(x, br)
+    torch.cuda.synchronize()
+    for blk in (0, 1, rows // br // 2, rows // br - 1):
+        r0 = blk * br
+        xs = x[r0:r0 + br].cpu().numpy()
+        oq, os_ = orc.quantize(xs, br)
+        assert np.array_equal(q[r0:r0 + br].cpu().numpy(), oq), blk
+        got_s = s[:, blk:blk + 1].cpu().numpy()
+        assert np.array_equal(got_s.view(np.uint32), os_.view(np.uint32)), blk
+    bad = torch.empty((rows + (32 if br == 1 else 128), cols), device="cuda")
+    qb = torch.empty(bad.shape, dtype=torch.uint8, device="cuda")
+    sb = torch.empty((-(-cols // 128), bad.shape[0] // br), device="cuda")
+    with pytest.raises(dg.DGError):
+        dg.dg_quantize_fp8_block(qb, sb, bad, br)
