@@ -66,7 +66,8 @@ int dg_get_mk_alignment_for_contiguous_layout(void);
  * For each block: amax = max|x|; s = amax / 448 (binary32 division);
  * s == 0 (all-zero block) gives codes +-0 with the element's sign; otherwise
  * q = round-to-nearest-even-E4M3(binary32(x / s)), saturating at 448.
- * Requirements: rows >= 1, cols >= 1, cols % 16 == 0.
+ * Requirements: rows >= 1, cols >= 1, cols % 16 == 0; rows <= 65535 * 128
+ * (block_rows 128) or 65535 * 32 (block_rows 1), else DG_ERR_SHAPE.
  */
 int dg_quantize_fp8_block(uint8_t *q, float *scales, const float *x,
                           int64_t rows, int64_t cols, int block_rows, void *stream);
@@ -89,8 +90,14 @@ size_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   sb : FP32 [K/128][ceil(N/128)] (128x128 blocks).
  *   workspace / workspace_bytes: optional device scratch for split-K on
  *        small-M shapes (see dg_fp8_gemm_nt_workspace_bytes); may be NULL/0.
- *        Its contents need not be initialised and are clobbered.
- * Requirements: M >= 1; N >= 8, N % 8 == 0; K >= 128, K % 128 == 0.
+ *        Its contents need not be initialised and are clobbered.  A split-K
+ *        plan also uses a library-owned array of per-tile arrival counters
+ *        on the device, which every call leaves zeroed: two split-K calls
+ *        that run at the same time on one GPU (different streams) race on
+ *        it, so such calls must be ordered (or given no workspace).
+ * Requirements: M >= 1; N >= 8, N % 8 == 0; K >= 128, K % 128 == 0;
+ * M*K and N*K below 2^32 (byte offsets inside the kernels are 32-bit),
+ * else DG_ERR_SHAPE.
  * The result is deterministic: a given plan sums in a fixed order.
  */
 int dg_fp8_gemm_nt(uint16_t *c, const uint8_t *a, const uint8_t *b,
@@ -112,8 +119,9 @@ int dg_fp8_gemm_nt(uint16_t *c, const uint8_t *a, const uint8_t *b,
  * Row m computes C[m] = A[m] . B[g]^T with g = m_indices[m], scales as in
  * dg_fp8_gemm_nt using sb + g * (K/128) * ceil(N/128).
  * Requirements: M >= 128, M % 128 == 0; N >= 8, N % 8 == 0; K % 128 == 0;
- * 1 <= num_groups.  Ids outside [-1, num_groups) are a contract violation
- * (such rows are written as zeros).
+ * 1 <= num_groups; M*K and N*K below 2^32.  Ids outside [-1, num_groups)
+ * are a contract violation (a block whose first row holds one is written as
+ * zeros; elsewhere the result is unspecified).
  */
 int dg_fp8_grouped_gemm_contig(uint16_t *c, const uint8_t *a, const uint8_t *b,
                                const float *sa, const float *sb, int a_block_rows,
