@@ -104,6 +104,27 @@ class Timer:
             self.graphs[key] = g
         return self.graphs[key]
 
+    def stats(self, fn, reps: int, key, calls: int = 4, warmup: int = 3) -> dict:
+        """Per-launch microseconds over `reps` replays of a graph of `calls`
+        back-to-back launches (events around each replay): mean, median, min."""
+        def body():
+            for _ in range(calls):
+                fn()
+        g = self.graph((key, calls), body)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for s, e in ev:
+            s.record(self.stream)
+            g.replay()
+            e.record(self.stream)
+        torch.cuda.synchronize()
+        us = sorted(s.elapsed_time(e) * 1e3 / calls for s, e in ev)
+        return {"mean": sum(us) / len(us), "median": us[len(us) // 2], "min": us[0],
+                "launches": reps * calls, "warmup_launches": warmup * calls}
+
     def time(self, fn, reps: int, key=None, calls: int = 1) -> float:
         """Milliseconds per call of fn (fn may enqueue several kernels).
 
@@ -217,7 +238,12 @@ class Dense:
     def roofline(self, timer, reps):
         """Dominant kernel: the GEMM launch on the largest shape (8192^3)."""
         n, it = max(enumerate(self.items), key=lambda t: t[1]["M"] * t[1]["N"] * t[1]["K"])
-        t = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
+        if timer.use_graph:
+            st = timer.stats(lambda: self.gemm(it), max(reps, 25), ("g", n), calls=4)
+            t = st["mean"] * 1e-3
+        else:
+            st = None
+            t = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
         flop = 2.0 * it["M"] * it["N"] * it["K"]
         ach = flop / (t * 1e-3) / 1e12
         key = "gemm_tiled_kernel<256,%d,false> %dx%dx%d" % (self.a_br, it["M"], it["N"], it["K"])
@@ -226,37 +252,58 @@ class Dense:
                 "traffic": recorded_traffic(key, GEMM_TILED_SOURCES),
                 "algorithmic_bytes": it["M"] * it["K"] + it["N"] * it["K"] + 2 * it["M"] * it["N"]
                 + 4 * (it["K"] // 128) * (cdiv(it["M"], self.a_br) + cdiv(it["N"], 128)),
-                "avg_launch_us": t * 1e3}
+                "avg_launch_us": t * 1e3, "launch_us_stats": st}
 
     def cpu_baseline(self):
-        """The oracle (single thread, plain C) on a bounded sample: per shape,
-        quantise all of B and one 128-row block of A, and compute 4 full
-        output rows; extrapolated to the whole step (B quantised once, A in
-        M/128 blocks, M output rows)."""
+        """The oracle (plain C, one call per thread over disjoint rows) on a
+        bounded sample, timed on the host's cores: per shape, quantise all of
+        B (split at 128-row block boundaries, one slice per thread) and one
+        128-row block of A, and compute 8 full output rows per thread.
+        Extrapolated to the whole step on the same threads (B quantised once,
+        A in M/128 blocks, M output rows)."""
+        import concurrent.futures as cf
         import oracle
-        rows = 4
+        threads = max(1, min(16, os.cpu_count() or 1))
+        rows_per_thread = 8
+        oracle.e4m3_decode(np.zeros(1, np.uint8))      # load the library before threading
         total = 0.0
         spent = 0.0
-        for it in self.items:
-            M, N, K = it["M"], it["N"], it["K"]
-            a = it["a"][:128].cpu().numpy()
-            b = it["b"].cpu().numpy()
-            t0 = time.perf_counter()
-            qb, sb = oracle.quantize(b, 128)
-            t1 = time.perf_counter()
-            qa, sa = oracle.quantize(a, self.a_br)
-            t2 = time.perf_counter()
-            ii = np.repeat(np.linspace(0, 127, rows).astype(np.int64), N)
-            jj = np.tile(np.arange(N, dtype=np.int64), rows)
-            oracle.gemm_nt_points(qa, sa, qb, sb, ii, jj, a_block_rows=self.a_br)
-            t3 = time.perf_counter()
-            spent += t3 - t0
-            total += (t1 - t0) + (M / 128) * (t2 - t1) + (M / rows) * (t3 - t2)
-        return {"value": self.flops / total / 1e12, "unit": "TFLOP/s", "cores": 1,
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            for it in self.items:
+                M, N, K = it["M"], it["N"], it["K"]
+                a = it["a"][:128].cpu().numpy()
+                b = it["b"].cpu().numpy()
+                nblk = cdiv(N, 128)
+                cuts = [min(N, 128 * (nblk * t // threads)) for t in range(threads + 1)]
+                t0 = time.perf_counter()
+                parts = list(ex.map(lambda t: oracle.quantize(b[cuts[t]:cuts[t + 1]], 128)
+                                    if cuts[t + 1] > cuts[t] else None, range(threads)))
+                t1 = time.perf_counter()
+                qb = np.concatenate([p[0] for p in parts if p is not None])
+                sb = np.concatenate([p[1] for p in parts if p is not None], axis=1)
+                t1b = time.perf_counter()
+                qa, sa = oracle.quantize(a, self.a_br)
+                t2 = time.perf_counter()
+                rows = np.linspace(0, 127, threads * rows_per_thread).astype(np.int64)
+
+                def gemm_rows(t):
+                    r = rows[t * rows_per_thread:(t + 1) * rows_per_thread]
+                    return oracle.gemm_nt_points(qa, sa, qb, sb, np.repeat(r, N),
+                                                 np.tile(np.arange(N, dtype=np.int64), r.size),
+                                                 a_block_rows=self.a_br)
+                t2b = time.perf_counter()
+                list(ex.map(gemm_rows, range(threads)))
+                t3 = time.perf_counter()
+                spent += (t1 - t0) + (t2 - t1b) + (t3 - t2b)
+                total += ((t1 - t0) + (M / 128) * (t2 - t1b) / threads
+                          + (M / (threads * rows_per_thread)) * (t3 - t2b))
+        return {"value": self.flops / total / 1e12, "unit": "TFLOP/s", "cores": threads,
                 "kind": "oracle",
-                "sample": "per shape: oracle quantise of all of B and one 128-row block of A, "
-                          "%d full output rows of the FP64 dequantised GEMM (%.1f s of CPU "
-                          "time); extrapolated to the full step (%.0f s)" % (rows, spent, total)}
+                "sample": "per shape: oracle quantise of all of B (%d threads, one slice of "
+                          "128-row blocks each) and of one 128-row block of A, then %d full "
+                          "output rows of the FP64 dequantised GEMM per thread (%.1f s wall); "
+                          "extrapolated to the full step on the same threads (%.0f s)"
+                          % (threads, rows_per_thread, spent, total)}
 
 
 class Decode:
@@ -398,6 +445,34 @@ class Moe:
         return None
 
 
+def dpm_clocks():
+    """Current shader and memory clock levels (MHz) from the amdgpu sysfs DPM
+    tables of the card torch uses, or None where they are not readable."""
+    import glob
+    try:
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+    except Exception:
+        bus = None
+    cards = sorted(glob.glob("/sys/class/drm/card[0-9]*/device"))
+    if bus is not None:
+        cards = [c for c in cards if os.path.realpath(c).split("/")[-1].split(":")[-2:-1] ==
+                 ["%02x" % bus]] or cards
+    for c in cards:
+        out = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(c, name)) as f:
+                    cur = [ln for ln in f.read().splitlines() if ln.strip().endswith("*")]
+            except OSError:
+                cur = []
+            if cur:
+                out[name[-4:]] = cur[0].split(":", 1)[1].strip(" *")
+        if out:
+            out["card"] = os.path.basename(os.path.dirname(c))
+            return out
+    return None
+
+
 def measured_mfma_peak(blocks=1024, iters=10000, reps=3):
     """Dense FP8 matrix-core rate this GPU sustains on a pure MFMA loop
     (4 waves per SIMD, 8 independent 16x16x128 chains per wave, pseudo-random
@@ -535,6 +610,7 @@ def main():
                 break
         rounds = cdiv(args.steps, w.rot)
     steps = rounds * w.rot if use_graph else args.steps
+    clocks_before = dpm_clocks()
     log("timing", steps, "steps", "(graph)" if use_graph else "(eager)")
     t0 = time.perf_counter()
     if use_graph:
@@ -542,6 +618,7 @@ def main():
     else:
         ms = timer.time(w.step, steps)
     wall = time.perf_counter() - t0
+    clocks_after = dpm_clocks()
     log("step %.4f ms (wall %.2f s)" % (ms, wall))
 
     breakdown = w.breakdown(timer, args.kernel_reps)
@@ -564,7 +641,8 @@ def main():
            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)", "data": "synthetic",
            "config": dict(w.config(), timing="hip graph replay" if use_graph else "eager"),
-           "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown}
+           "roofline": roof, "cpu_baseline": cpu, "breakdown": breakdown,
+           "clocks": {"before": clocks_before, "after": clocks_after}}
     print(json.dumps(rec), flush=True)
 
 
