@@ -339,31 +339,56 @@ class Decode:
                                workspace=it["ws"])
 
     def step(self, i=0):
+        # M <= 16: one call quantises A inside the GEMM (same codes and scales);
+        # larger M: quantiser, then GEMM
         for it in self.items:
-            self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
-            self.gemm(it, i)
+            if it["M"] <= self.dg.FUSED_A_MAX_M:
+                self.fused(it, i)
+            else:
+                self.quantise_and_gemm(it, i)
 
     def outputs(self):
-        return [t for it in self.items for t in (it["qa"], it["sa"], it["c"])]
+        out = []
+        for it in self.items:
+            out += [it["c"]] if it["M"] <= self.dg.FUSED_A_MAX_M else [it["qa"], it["sa"], it["c"]]
+        return out
 
     def config(self):
         return {"workload": "decode-shaped GEMMs, M in {1,16,64} x (N,K) in {(24576,1536),"
                             "(7168,16384),(4096,4096)}, A 1x128 scales, B 128x128 scales",
-                "step": "quantise A + GEMM per shape; weights rotated over >768 MB of copies"}
+                "step": "quantise A + GEMM per shape (M <= 16: one call that quantises A "
+                        "inside the GEMM); weights rotated over >768 MB of copies"}
 
     def _time_gemm(self, timer, n, it, reps):
         rot = it["copies"]
         return timer.time(lambda: [self.gemm(it, i) for i in range(rot)], reps,
                           key=("dec", n)) / rot
 
+    def quantise_and_gemm(self, it, i):
+        self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
+        self.gemm(it, i)
+
+    def fused(self, it, i):
+        j = i % it["copies"]
+        self.dg.dg_fp8_gemm_nt_fused_a(it["c"], it["a"], it["qb"][j], it["sb"][j],
+                                       workspace=it["ws"])
+
     def breakdown(self, timer, reps):
         out = []
         for n, it in enumerate(self.items):
             t = self._time_gemm(timer, n, it, reps)
             b = self.bytes_of(it)
-            out.append({"mnk": [it["M"], it["N"], it["K"]], "gemm_us": t * 1e3,
-                        "hbm_gbs": b / (t * 1e-3) / 1e9,
-                        "hbm_frac": b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS})
+            row = {"mnk": [it["M"], it["N"], it["K"]], "gemm_us": t * 1e3,
+                   "hbm_gbs": b / (t * 1e-3) / 1e9,
+                   "hbm_frac": b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            rot = it["copies"]
+            row["quantise_gemm_us"] = timer.time(
+                lambda: [self.quantise_and_gemm(it, i) for i in range(rot)], reps,
+                key=("decq", n)) / rot * 1e3
+            if it["M"] <= self.dg.FUSED_A_MAX_M:
+                row["fused_us"] = timer.time(lambda: [self.fused(it, i) for i in range(rot)],
+                                             reps, key=("decf", n)) / rot * 1e3
+            out.append(row)
         return out
 
     def roofline(self, timer, reps):

@@ -35,7 +35,7 @@ class DGError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libdg.so not built (%s); run `python -m fp8_block_scaled_dg_amd.build`"
+        raise ImportError("libdg.so not built (%s); run `python fp8_block_scaled_dg_amd/build.py`"
                           % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -51,6 +51,9 @@ def _load():
     lib.dg_fp8_gemm_nt_workspace_bytes.argtypes = [i64, i64, i64]
     lib.dg_fp8_gemm_nt.restype = i32
     lib.dg_fp8_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.dg_fp8_gemm_nt_fused_a.restype = i32
+    lib.dg_fp8_gemm_nt_fused_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t,
+                                           vp]
     lib.dg_fp8_grouped_gemm_contig.restype = i32
     lib.dg_fp8_grouped_gemm_contig.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
     if lib.dg_abi_version() != ABI_VERSION:
@@ -109,6 +112,14 @@ def _bf16(t, name):
     return t
 
 
+def _workspace_bytes(workspace) -> int:
+    if workspace is None:
+        return 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.numel() * workspace.element_size()
+
+
 def cdiv(a: int, b: int) -> int:
     return (a + b - 1) // b
 
@@ -153,14 +164,33 @@ def dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows: int = 128, workspace=None,
         raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
     if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
         raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
-    ws_bytes = 0
-    if workspace is not None:
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous device tensor")
-        ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _workspace_bytes(workspace)
     _check(lib.dg_fp8_gemm_nt(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), a_block_rows,
                               M, N, K, _ptr(workspace), ws_bytes, _stream(stream)),
            "dg_fp8_gemm_nt")
+
+
+FUSED_A_MAX_M = 16
+
+
+def dg_fp8_gemm_nt_fused_a(c, a, b, sb, workspace=None, stream=None) -> None:
+    """C[M,N] (bf16) = A[M,K] (float32, quantised with 1x128 blocks inside the
+    GEMM) . B[N,K]^T (E4M3, 128x128 scales sb); M <= FUSED_A_MAX_M."""
+    c = _bf16(c, "c")
+    _require(a, torch.float32, "a")
+    b = _codes(b, "b")
+    _require(sb, torch.float32, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or c.shape != (M, N):
+        raise ValueError("shape mismatch: a %s, b %s, c %s" % (tuple(a.shape), tuple(b.shape),
+                                                              tuple(c.shape)))
+    if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
+    ws_bytes = _workspace_bytes(workspace)
+    _check(lib.dg_fp8_gemm_nt_fused_a(_ptr(c), _ptr(a), _ptr(b), _ptr(sb), M, N, K,
+                                      _ptr(workspace), ws_bytes, _stream(stream)),
+           "dg_fp8_gemm_nt_fused_a")
 
 
 def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices,
@@ -214,5 +244,5 @@ def fp8_grouped_gemm_contig(c, a, b, sa, sb, m_indices, a_block_rows: int = 1):
 __all__ = [
     "lib", "LIB_PATH", "DGError", "status_string", "get_mk_alignment_for_contiguous_layout",
     "dg_quantize_fp8_block", "dg_fp8_gemm_nt_workspace_bytes", "dg_fp8_gemm_nt",
-    "dg_fp8_grouped_gemm_contig", "to_fp8", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
+    "dg_fp8_gemm_nt_fused_a", "FUSED_A_MAX_M", "dg_fp8_grouped_gemm_contig", "to_fp8", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
 ]

@@ -1,6 +1,6 @@
 """Build libdg.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
-    python -m fp8_block_scaled_dg_amd.build
+    python fp8_block_scaled_dg_amd/build.py
 
 Every source is compiled for gfx950 only.  Packed-FP32 VALU forms are
 disabled (-packed-fp32-ops) for all device code.

@@ -32,6 +32,20 @@ int check_gemm(const uint16_t* c, const uint8_t* a, const uint8_t* b, const floa
   return DG_OK;
 }
 
+// A split-K workspace, when given, must hold what the small-M plan for this
+// shape uses and be 16-byte aligned; a NULL pointer or a zero size means none.
+int check_workspace(int64_t M, int64_t N, int64_t K, void** workspace, size_t* workspace_bytes) {
+  if (*workspace != nullptr && *workspace_bytes > 0) {
+    const size_t need = dg::skinny_applies(M, N, K) ? dg::skinny_workspace_bytes(M, N, K) : 0;
+    if (*workspace_bytes < need) return DG_ERR_WORKSPACE;
+    if (!aligned(*workspace, 16)) return DG_ERR_ALIGN;
+  } else {
+    *workspace = nullptr;  // one of the two missing: treat as "no workspace"
+    *workspace_bytes = 0;
+  }
+  return DG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,14 +92,8 @@ int dg_fp8_gemm_nt(uint16_t* c, const uint8_t* a, const uint8_t* b, const float*
   int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
   if (st != DG_OK) return st;
   const bool skinny = dg::skinny_applies(M, N, K);
-  if (workspace != nullptr && workspace_bytes > 0) {
-    const size_t need = skinny ? dg::skinny_workspace_bytes(M, N, K) : 0;
-    if (workspace_bytes < need) return DG_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return DG_ERR_ALIGN;
-  } else if (workspace != nullptr || workspace_bytes > 0) {
-    workspace = nullptr;  // one of the two missing: treat as "no workspace"
-    workspace_bytes = 0;
-  }
+  st = check_workspace(M, N, K, &workspace, &workspace_bytes);
+  if (st != DG_OK) return st;
   dg::GemmProblem p{c, a, b, sa, sb, nullptr, 1, a_block_rows, M, N, K};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (skinny) {
@@ -95,6 +103,23 @@ int dg_fp8_gemm_nt(uint16_t* c, const uint8_t* a, const uint8_t* b, const float*
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles > INT32_MAX) return DG_ERR_SHAPE;
   return from_hip(dg::launch_gemm_tiled(p, false, s));
+}
+
+int dg_fp8_gemm_nt_fused_a(uint16_t* c, const float* a, const uint8_t* b, const float* sb,
+                           int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!c || !a || !b || !sb) return DG_ERR_NULL;
+  if (M < 1 || M > DG_FUSED_A_MAX_M || N < 8 || K < 128) return DG_ERR_SHAPE;
+  if (N % 8 != 0 || K % 128 != 0) return DG_ERR_SHAPE;
+  if (N > INT32_MAX || K > INT32_MAX || N * K > kU32) return DG_ERR_SHAPE;
+  if (!dg::skinny_applies(M, N, K)) return DG_ERR_SHAPE;
+  if (!aligned(c, 16) || !aligned(a, 16) || !aligned(b, 16) || !aligned(sb, 4))
+    return DG_ERR_ALIGN;
+  const int st = check_workspace(M, N, K, &workspace, &workspace_bytes);
+  if (st != DG_OK) return st;
+  dg::GemmProblem p{c, nullptr, b, nullptr, sb, nullptr, 1, 1, M, N, K};
+  return from_hip(dg::launch_gemm_skinny_fused_a(p, a, workspace, workspace_bytes,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int dg_fp8_grouped_gemm_contig(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,

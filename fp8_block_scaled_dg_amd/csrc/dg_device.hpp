@@ -33,4 +33,81 @@ __device__ __forceinline__ float half_wave_max(float v) {
   return v;
 }
 
+// ---- E4M3 block encoding, shared by the quantiser and the GEMM that
+// quantises its activations on the fly (FP8 block-quantised GEMM page on
+// lpnh.cn, s4.2 steps 3-4 and the RNE note; s5.4 for all-zero blocks) ----
+
+// Per-block scale s = amax / 448 (one binary32 division; the stored scale)
+// and what the quotients x / s are formed from: k = 1, or 2^64 when s < 2^-62
+// (sk = s k and x k are then exact, so (x k) / sk = x / s), and r = RN(1/sk)
+// (0 for an all-zero block, s = 0).
+struct BlockScale {
+  float s, k, sk, r;
+};
+
+__device__ __forceinline__ BlockScale block_scale(float amax) {
+  BlockScale b;
+  b.s = amax / 448.0f;
+  b.k = b.s < 0x1p-62f ? 0x1p64f : 1.0f;
+  b.sk = b.s * b.k;
+  b.r = b.s == 0.0f ? 0.0f : 1.0f / b.sk;
+  return b;
+}
+
+// Correctly rounded binary32 quotient x / s from r = RN(1/s) and one FMA
+// correction (Markstein: q = RN(x r), q' = RN(q + (x - q s) r) = RN(x/s)
+// provided the remainder x - q s is exact).  The remainder is a multiple of
+// ulp(q) ulp(s); for quotients >= 2^-11 (smaller ones encode to zero either
+// way) and s >= 2^-62 that is >= 2^-119, inside binary32's range, so the
+// remainder is representable.  Smaller scales, subnormal ones included, are
+// lifted by 2^64 first (block_scale).
+__device__ __forceinline__ float quotient_rn(float x, float s, float r) {
+  const float q = x * r;
+  const float e = __builtin_fmaf(-q, s, x);
+  return __builtin_fmaf(e, r, q);
+}
+
+// |x| / s, correctly rounded, capped at 448.  The quotient is formed on |x|
+// (s > 0, so |x/s| = |x|/s) and the sign bit is restored by the caller: the
+// FMA correction would turn a -0 quotient into +0.  Quotients above 448 round
+// to 448 in E4M3 anyway (saturation).  In an all-zero block (sk = r = 0)
+// every step yields 0.
+__device__ __forceinline__ float magnitude_quotient(float x, const BlockScale& b) {
+  return fminf(quotient_rn(fabsf(x) * b.k, b.sk, b.r), 448.0f);
+}
+
+// Sign bits of four values placed at bit 7 of each code byte.
+__device__ __forceinline__ uint32_t zero_codes4(float4 v) {
+  return ((__float_as_uint(v.x) >> 31) << 7) | ((__float_as_uint(v.y) >> 31) << 15) |
+         ((__float_as_uint(v.z) >> 31) << 23) | ((__float_as_uint(v.w) >> 31) << 31);
+}
+
+// Codes of four values of a block with scale b: round to the nearest E4M3
+// code, ties to even, with v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950, default
+// round-to-nearest-even mode), then OR in the sign bits.  The instruction's
+// result was compared on an MI355X with a ties-to-even encoder written from
+// the E4M3 field layout, for every binary32 magnitude below 464 and both
+// signs (including binary32 subnormals and -0): no difference.  Branch-free.
+__device__ __forceinline__ uint32_t encode4_block(float4 v, const BlockScale& b) {
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(magnitude_quotient(v.x, b), magnitude_quotient(v.y, b),
+                                          0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(magnitude_quotient(v.z, b), magnitude_quotient(v.w, b), p,
+                                      true);
+  return (uint32_t)p | zero_codes4(v);
+}
+
+__device__ __forceinline__ float abs_max4(float m, float4 v) {
+  return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+// Maximum over each row of 16 lanes (lanes 16i .. 16i+15), with DPP moves:
+// swap neighbours, swap pairs, mirror each half-row, mirror the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 }  // namespace dg

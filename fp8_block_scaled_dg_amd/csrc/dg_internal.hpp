@@ -31,6 +31,10 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
 bool skinny_applies(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const GemmProblem& p, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+// The same kernel with A given in FP32 (M <= 16) and quantised with 1x128
+// blocks as it is staged; p.a and p.sa are unused.  128-row B tiles.
+hipError_t launch_gemm_skinny_fused_a(const GemmProblem& p, const float* af, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 // Streaming small-M kernel (no workspace), and whether it is the better of
 // the two small-M kernels for a shape.

@@ -48,6 +48,7 @@ __device__ int g_splitk_counters[kMaxCounters];
 struct SkinnyArgs {
   uint16_t* c;
   const uint8_t* a;
+  const float* af;  // FP32 A when the kernel quantises A itself, else null
   const uint8_t* b;
   const float* sa;
   const float* sb;
@@ -71,23 +72,37 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
   return r;
 }
 
-template <int MP, int F>
+// AF32: A arrives as FP32 (M <= 16) and the workgroup quantises it with 1x128
+// blocks: each stage also carries the FP32 A block (16 rows x 128 values,
+// rows past M clamped), fetched by the same LDS DMA as B.  After the step's
+// barrier, thread t encodes values [4j, 4j + 4) and [64 + 4j, 64 + 4j + 4) of
+// row t/16 (j = t%16), the 16 threads of a row share the row's amax through
+// lane exchanges, the codes (in the layout the A DMA produces) and the row
+// scales go to a code buffer, and a second barrier publishes them to the
+// MFMAs.  FP32 A is staged through LDS rather than registers: the compiler
+// waits for every load in flight before using a register loaded ahead of LDS
+// DMA instructions, which would drain the ring each step.
+template <int MP, int F, bool AF32 = false>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
+  static_assert(!AF32 || MP == 16, "in-kernel quantisation covers up to 16 rows");
   constexpr int BNT = 64 * F;                     // B rows per workgroup (F fragments per wave)
   constexpr int MPE = MP < 32 ? 32 : MP;          // A rows staged (>= 4 DMA instructions)
   constexpr int B_BYTES = BNT * BK;               // 8 or 16 KB
-  constexpr int A_BYTES = MPE * BK;
-  constexpr int SA_BYTES = 4 * 256;               // one 64-float copy per wave
+  constexpr int A_BYTES = AF32 ? 16 * BK * 4 : MPE * BK;  // FP32 A (AF32) or E4M3 A
+  constexpr int SA_BYTES = AF32 ? 0 : 4 * 256;    // one 64-float copy per wave
   constexpr int SB_BYTES = 4 * 256;               // B block scale (64 copies) per wave
   constexpr int STAGE = B_BYTES + A_BYTES + SA_BYTES + SB_BYTES;
   constexpr int B_IT = B_BYTES / 1024 / 4;        // DMA instructions per wave per stage
   constexpr int A_IT = A_BYTES / 1024 / 4;
-  constexpr int PER_STAGE = B_IT + A_IT + 2;      // + the A scale row + the B scale
+  constexpr int PER_STAGE = B_IT + A_IT + (AF32 ? 1 : 2);  // + the A scale row + the B scale
   constexpr int NI = MP / 16;                     // A fragments
   static_assert(NS == 3, "the ring below is written out for three slots");
   __shared__ __attribute__((aligned(1024))) uint8_t l0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t l1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t l2[STAGE];
+  // AF32 code buffer: 16 rows x 128 codes, then the 16 row scales (never a
+  // DMA target, so stores to it need no wait on the DMA in flight)
+  __shared__ __attribute__((aligned(128))) uint8_t qb[AF32 ? 16 * BK + 16 * 4 : 16];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
@@ -103,6 +118,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   // 1 KB at LDS offset (j*4 + w)*1024 of the B (or A) region: rows 8*(j*4+w)
   // .. +7, lane L -> row +L/8, physical chunk L%8.
   uint32_t boff[B_IT], aoff[A_IT];
+  const float* a32[AF32 ? A_IT : 1];  // AF32: instruction j's FP32 A row chunk at kb = 0
 #pragma unroll
   for (int j = 0; j < B_IT; ++j) {
     const int r = (j * 4 + wave) * 8 + (lane >> 3);
@@ -112,9 +128,17 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   }
 #pragma unroll
   for (int j = 0; j < A_IT; ++j) {
-    const int r = (j * 4 + wave) * 8 + (lane >> 3);
-    const int gr = r < p.M ? r : p.M - 1;
-    aoff[j] = (uint32_t)gr * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ lds_swz(r)) * 16);
+    if constexpr (AF32) {
+      // 1 KB = two 512-byte FP32 rows: lane L -> row +L/32, bytes 16*(L%32)
+      const int r = (j * 4 + wave) * 2 + (lane >> 5);
+      const int gr = r < p.M ? r : p.M - 1;
+      a32[j] = p.af + (int64_t)gr * p.K + (lane & 31) * 4;
+      aoff[j] = 0;
+    } else {
+      const int r = (j * 4 + wave) * 8 + (lane >> 3);
+      const int gr = r < p.M ? r : p.M - 1;
+      aoff[j] = (uint32_t)gr * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ lds_swz(r)) * 16);
+    }
   }
   const int sa_row = p.a_block_rows == 1 ? (lane < p.M ? lane : p.M - 1) : 0;
   const int nb = n0 / 128;  // the 128 rows of this workgroup form one B scale block
@@ -126,17 +150,49 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
       __builtin_amdgcn_global_load_lds((const void*)(p.b + boff[j] + (uint32_t)kb * BK),
                                        (__attribute__((address_space(3))) void*)(st + (j * 4 + wave) * 1024),
                                        16, 0, 0);
+    if constexpr (AF32) {
 #pragma unroll
-    for (int j = 0; j < A_IT; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(p.a + aoff[j] + (uint32_t)kb * BK),
-                                       (__attribute__((address_space(3))) void*)(st + B_BYTES + (j * 4 + wave) * 1024),
-                                       16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(p.sa + (int64_t)kb * p.sa_stride + sa_row),
-                                     (__attribute__((address_space(3))) void*)(st + B_BYTES + A_BYTES + wave * 256),
-                                     4, 0, 0);
+      for (int j = 0; j < A_IT; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(a32[j] + (int64_t)kb * BK),
+                                         (__attribute__((address_space(3))) void*)(st + B_BYTES + (j * 4 + wave) * 1024),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < A_IT; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(p.a + aoff[j] + (uint32_t)kb * BK),
+                                         (__attribute__((address_space(3))) void*)(st + B_BYTES + (j * 4 + wave) * 1024),
+                                         16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(p.sa + (int64_t)kb * p.sa_stride + sa_row),
+                                       (__attribute__((address_space(3))) void*)(st + B_BYTES + A_BYTES + wave * 256),
+                                       4, 0, 0);
+    }
     __builtin_amdgcn_global_load_lds((const void*)(p.sb + (int64_t)kb * p.sb_stride + nb),
                                      (__attribute__((address_space(3))) void*)(st + B_BYTES + A_BYTES + SA_BYTES + wave * 256),
                                      4, 0, 0);
+  };
+
+  // in-kernel quantisation of A (AF32): row qr, values [4qj, 4qj + 4) and
+  // [64 + 4qj, 64 + 4qj + 4) of the staged block (conflict-free LDS reads)
+  const int qr = threadIdx.x >> 4;
+  const int qj = threadIdx.x & 15;
+  auto quantise_a = [&](const uint8_t* st) {
+    // read as integers: a float-typed LDS read makes the compiler wait for
+    // every DMA in flight (it cannot tell it from the ring's other slots)
+    const v4i i0 = *reinterpret_cast<const v4i*>(st + B_BYTES + qr * 512 + 16 * qj);
+    const v4i i1 = *reinterpret_cast<const v4i*>(st + B_BYTES + qr * 512 + 256 + 16 * qj);
+    const float4 v0 = make_float4(__int_as_float(i0[0]), __int_as_float(i0[1]),
+                                  __int_as_float(i0[2]), __int_as_float(i0[3]));
+    const float4 v1 = make_float4(__int_as_float(i1[0]), __int_as_float(i1[1]),
+                                  __int_as_float(i1[2]), __int_as_float(i1[3]));
+    const BlockScale bs = block_scale(row16_max(abs_max4(abs_max4(0.0f, v0), v1)));
+    // code byte k of row qr sits in logical 16-byte chunk k/16, at physical
+    // chunk (k/16) ^ swz(qr)
+    const int sw = lds_swz(qr);
+    *reinterpret_cast<uint32_t*>(qb + qr * 128 + (((qj >> 2) ^ sw) * 16) + (qj & 3) * 4) =
+        encode4_block(v0, bs);
+    *reinterpret_cast<uint32_t*>(qb + qr * 128 + ((((qj >> 2) + 4) ^ sw) * 16) + (qj & 3) * 4) =
+        encode4_block(v1, bs);
+    if (qj == 0) reinterpret_cast<float*>(qb + 16 * BK)[qr] = bs.s;
   };
 
   const int fr = lane & 15;
@@ -157,9 +213,11 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   // (the slot of stage it-1, free once every wave has passed this barrier)
   auto body = [&](int it, const uint8_t* cur, uint8_t* nxt) {
     // this wave's loads for stage `it` have landed once at most the loads of
-    // the NS-2 younger stages remain outstanding (loads retire in order)
+    // the NS-2 younger stages remain outstanding (loads retire in order); with
+    // AF32 its reads of the previous step's codes have completed too
+    // (lgkmcnt 0), so after the barrier the code buffer may be rewritten
     __builtin_amdgcn_s_waitcnt((((NS - 2) * PER_STAGE) & 15) | ((((NS - 2) * PER_STAGE) >> 4) << 14) |
-                               (0x7 << 4) | (0xF << 8));
+                               (0x7 << 4) | ((AF32 ? 0x0 : 0xF) << 8));
     // A bare barrier: __syncthreads() adds a workgroup release fence, which
     // waits for every outstanding DMA write to LDS (all NS-1 stages in
     // flight).  Every wave has waited for its own loads of stage `it` above,
@@ -167,20 +225,27 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     // so the barrier alone makes stage `it` complete and slot it-1 free.
     asm volatile("s_barrier" ::: "memory");
     issue_stage(it + NS - 1, nxt);
+    if constexpr (AF32) {
+      quantise_a(cur);
+      // the codes are complete (lgkmcnt 0) and visible to every wave
+      __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+      asm volatile("s_barrier" ::: "memory");
+    }
 
     // Steps past the K range (the unrolled ring always runs whole rounds of
     // three) re-read the last staged block with a zero scale: they add exactly
     // 0, and they keep the loop free of branches, without which the
     // compiler's LDS-DMA tracking falls back to waiting for every load.
-    const float sbv =
-        it < nk ? reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64] : 0.0f;
+    const float sbv_l = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64];
+    const float sbv = it < nk ? sbv_l : 0.0f;
     float s[NI];
-    const float* sa_l = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
+    const float* sa_l = AF32 ? reinterpret_cast<const float*>(qb + 16 * BK)
+                             : reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
 #pragma unroll
     for (int i = 0; i < NI; ++i) s[i] = sa_l[16 * i + fr] * sbv;  // (all 64 slots equal for 128-row A blocks)
     v8i af[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) af[i] = read_frag(cur + B_BYTES, 16 * i, off0, off1);
+    for (int i = 0; i < NI; ++i) af[i] = read_frag(AF32 ? qb : cur + B_BYTES, 16 * i, off0, off1);
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const v8i bf = read_frag(cur, wave * 16 * F + 16 * f, off0, off1);
@@ -375,10 +440,34 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  SkinnyArgs p;
+  p.c = q.c; p.a = nullptr; p.af = af; p.b = q.b; p.sa = nullptr; p.sb = q.sb;
+  p.a_block_rows = 1;
+  p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
+  p.nkb = (int)(q.K / BK);
+  p.sa_stride = p.M;
+  p.sb_stride = (int)((q.N + 127) / 128);
+  int S = choose_splits(q.M, q.N, q.K);
+  // Each step here also encodes A and waits at a second barrier, so short
+  // splits cost relatively more: keep >= 5 K blocks per split (measured on
+  // MI355X at N = K = 4096: 6 splits 9.4 / 10.5 us at M = 1 / 16, against
+  // 10.3 / 12.4 us with the 8 of the plain kernel's rule; N = 7168,
+  // K = 16384 keeps 8).  The workspace for the plain rule covers this.
+  if (forced_splits() == 0 && S > p.nkb / 5) S = p.nkb / 5 > 1 ? p.nkb / 5 : 1;
+  if (workspace == nullptr || workspace_bytes < skinny_workspace_bytes(q.M, q.N, q.K)) S = 1;
+  p.S = S;
+  p.partials = static_cast<float*>(workspace);
+  const unsigned grid = (unsigned)(((q.N + 127) / 128) * S);
+  hipLaunchKernelGGL((gemm_skinny_kernel<16, 2, true>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
   SkinnyArgs p;
-  p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.c = q.c; p.a = q.a; p.af = nullptr; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
   p.a_block_rows = q.a_block_rows;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
   p.nkb = (int)(q.K / BK);

@@ -106,6 +106,28 @@ int dg_fp8_gemm_nt(uint16_t *c, const uint8_t *a, const uint8_t *b,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * NT GEMM of FP32 activations with FP8 weights, the activations quantised
+ * inside the GEMM [Q s6: computing the scale factors inside the kernel saves
+ * a round trip through global memory; s4.2 for the quantisation]:
+ *   c  : out, BF16 [M][N] row-major, 16-byte aligned.
+ *   a  : FP32 [M][K] row-major, 16-byte aligned (never written).
+ *   b  : E4M3 [N][K] row-major, 16-byte aligned; sb: FP32 [K/128][ceil(N/128)].
+ * The result equals dg_quantize_fp8_block(a, block_rows = 1) followed by
+ * dg_fp8_gemm_nt(a_block_rows = 1): the codes and scales are the ones the
+ * quantiser would write, formed in registers and never stored.
+ *   workspace / workspace_bytes: optional split-K scratch, as for
+ *        dg_fp8_gemm_nt (size from dg_fp8_gemm_nt_workspace_bytes(M, N, K);
+ *        same counter rule for calls that overlap on one GPU).
+ * Requirements: 1 <= M <= DG_FUSED_A_MAX_M (small-batch decode); N >= 8,
+ * N % 8 == 0; K >= 128, K % 128 == 0; N*K below 2^32; else DG_ERR_SHAPE.
+ * Deterministic.
+ */
+#define DG_FUSED_A_MAX_M 16
+int dg_fp8_gemm_nt_fused_a(uint16_t *c, const float *a, const uint8_t *b, const float *sb,
+                           int64_t M, int64_t N, int64_t K,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Grouped GEMM, experts contiguous along M [D s2.3, s3.2, s3.3]:
  *   a         : E4M3 [M][K]; the rows of each expert are contiguous, experts
  *               in ascending id, each group padded to a multiple of 128 rows.

@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for need in ("dg_quantize_fp8_block", "dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contig",
                  "dg_abi_version", "dg_status_string", "dg_fp8_gemm_nt_workspace_bytes",
-                 "dg_get_mk_alignment_for_contiguous_layout"):
+                 "dg_get_mk_alignment_for_contiguous_layout", "dg_fp8_gemm_nt_fused_a"):
         assert need in names
 
 
@@ -111,3 +111,24 @@ def test_small_m_workspace_too_small_is_rejected(dg):
 def test_workspace_query_is_host_only(dg):
     assert dg.dg_fp8_gemm_nt_workspace_bytes(1, 4096, 4096) >= 0
     assert dg.dg_fp8_gemm_nt_workspace_bytes(0, 4096, 4096) == 0
+
+
+def gf(lib, c=P, a=P, b=P, sb=P, M=16, N=256, K=256, ws=None, wsb=0):
+    return lib.dg_fp8_gemm_nt_fused_a(c, a, b, sb, M, N, K, ws, wsb, None)
+
+
+def test_fused_a_validation(dg):
+    lib = dg.lib
+    for kw in ("c", "a", "b", "sb"):
+        assert gf(lib, **{kw: None}) == 1
+    assert gf(lib, M=0) == 2
+    assert gf(lib, M=dg.FUSED_A_MAX_M + 1) == 2   # decode batches only
+    assert gf(lib, N=4) == 2
+    assert gf(lib, N=260) == 2            # N % 8
+    assert gf(lib, K=200) == 2            # K % 128
+    assert gf(lib, N=65536, K=65536 + 128) == 2   # N*K >= 2^32
+    assert gf(lib, a=P1) == 4
+    assert gf(lib, sb=ctypes.c_void_p(0x10002)) == 4
+    need = dg.dg_fp8_gemm_nt_workspace_bytes(16, 4096, 4096)
+    assert gf(lib, M=16, N=4096, K=4096, ws=P, wsb=16) == 5
+    assert gf(lib, M=16, N=4096, K=4096, ws=P1, wsb=need) == 4

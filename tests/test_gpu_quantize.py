@@ -112,6 +112,46 @@ def test_quantize_every_midpoint_and_its_neighbours(dg, orc, amax):
         check(dg, orc, x, br, "midpoints amax=%g br=%d" % (amax, br))
 
 
+@pytest.mark.parametrize("amax_bits", [0x054FE4BA,    # s = amax/448 ~ 1.86 * 2^-126
+                                       0x05ABF09A,    # s ~ 1.27 * 2^-125
+                                       0x069A8AC6,    # s ~ 1.10 * 2^-123
+                                       0x13100000,    # s ~ 1.29 * 2^-98
+                                       0x04DBC887,    # s subnormal, ~1.96 * 2^-127
+                                       0x00C2A000])   # s subnormal, ~2^-135
+def test_quantize_midpoints_with_tiny_scales(dg, orc, amax_bits):
+    """Scales far below 1 that are not powers of two.  A quotient formed as
+    x * RN(1/s) plus one FMA correction is misrounded there when the
+    correction's remainder falls below binary32's smallest subnormal; the
+    first three blocks were picked because that formula, evaluated without
+    rescaling, gives a different E4M3 code than x / s for 14 to 19 of their
+    values.  Each block holds the amax, then the binary32 values nearest to
+    s times every E4M3 rounding midpoint and their neighbours two ulps either
+    way, both signs; codes and scales must match the oracle bit for bit."""
+    amax = np.array([amax_bits], np.uint32).view(np.float32)[0]
+    s = np.float32(amax / np.float32(448.0))
+    mags = np.array(sorted({float(v) for v in orc.e4m3_decode(np.arange(0x7F, dtype=np.uint8))}))
+    mids = (mags[:-1] + mags[1:]) / 2.0
+    vals = []
+    for m in mids:
+        v = np.float32(m * float(s))           # nearest binary32 to m*s
+        cand = [v]
+        for _ in range(2):
+            cand = [np.nextafter(cand[0], np.float32(0))] + cand + \
+                   [np.nextafter(cand[-1], np.float32(np.inf))]
+        for c in cand:
+            if np.abs(c) <= amax:
+                vals += [c, -c]
+    per_row = 127
+    rows = -(-len(vals) // per_row)
+    x = np.zeros((rows, 128), np.float32)
+    x[:, 0] = amax
+    flat = np.zeros(rows * per_row, np.float32)
+    flat[:len(vals)] = np.array(vals, np.float32)
+    x[:, 1:] = flat.reshape(rows, per_row)
+    for br in (1, 128):
+        check(dg, orc, x, br, "tiny scale, amax 0x%08x br=%d" % (amax_bits, br))
+
+
 @pytest.mark.parametrize("what,rows,cols,br", [
     ("C2a A", 4096, 2048, 128), ("C2c B", 8192, 8192, 128), ("C3 A M=64", 64, 16384, 1),
     ("C4 down A", 2816, 11008, 1)])
