@@ -70,6 +70,10 @@ def _load():
     lib.orc_e4m3_decode_n.argtypes = [u8p, f64p, i64]
     lib.orc_quantize_block.restype = ctypes.c_int
     lib.orc_quantize_block.argtypes = [f32p, i64, i64, ctypes.c_int, u8p, f32p]
+    lib.orc_quantize_block_ue8m0.restype = ctypes.c_int
+    lib.orc_quantize_block_ue8m0.argtypes = [f32p, i64, i64, ctypes.c_int, u8p, u8p]
+    lib.orc_ue8m0_pack.restype = None
+    lib.orc_ue8m0_pack.argtypes = [u8p, i64, i64, ctypes.POINTER(ctypes.c_uint32)]
     lib.orc_quantize_global.restype = ctypes.c_int
     lib.orc_quantize_global.argtypes = [f32p, i64, i64, u8p, f32p]
     lib.orc_gemm_nt.restype = ctypes.c_int
@@ -151,6 +155,40 @@ def quantize_global(x):
     if rc != 0:
         raise ValueError("oracle quantize_global rejected its input")
     return q, float(s[0])
+
+
+def quantize_ue8m0(x, block_rows: int = 128):
+    """Block quantiser with power-of-two scales (pzsr.cn DeepGEMM page s3.1,
+    UE8M0; the power of two is binary32(amax/448) rounded up -- see oracle.c).
+    x: float32 [rows, cols] -> (q uint8 [rows, cols],
+    exps uint8 [ceil(cols/128), ceil(rows/block_rows)], scale = 2^(E-127))."""
+    x = _c(x, np.float32)
+    assert x.ndim == 2
+    rows, cols = x.shape
+    q = np.empty((rows, cols), dtype=np.uint8)
+    e = np.empty((cdiv(cols, 128), cdiv(rows, block_rows)), dtype=np.uint8)
+    rc = _load().orc_quantize_block_ue8m0(_ptr(x, ctypes.c_float), rows, cols, block_rows,
+                                          _ptr(q, ctypes.c_uint8), _ptr(e, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle quantize_ue8m0 rejected its input")
+    return q, e
+
+
+def pack_ue8m0(exps) -> np.ndarray:
+    """uint8 [n_kb, n_rb] -> int32 [ceil(n_kb/4), n_rb], four exponents per word
+    along K blocks (byte kb % 4, least significant first; unused bytes 0)."""
+    e = _c(exps, np.uint8)
+    n_kb, n_rb = e.shape
+    out = np.empty((cdiv(n_kb, 4), n_rb), dtype=np.uint32)
+    _load().orc_ue8m0_pack(_ptr(e, ctypes.c_uint8), n_kb, n_rb, _ptr(out, ctypes.c_uint32))
+    return out.view(np.int32)
+
+
+def ue8m0_scales(exps) -> np.ndarray:
+    """Exponents -> float32 scales 2^(E-127) (exact: 2^-127 is a binary32
+    subnormal), for use with gemm_nt / gemm_nt_points."""
+    e = np.asarray(exps, dtype=np.int64)
+    return np.ldexp(np.float32(1.0), (e - 127).astype(np.int32)).astype(np.float32)
 
 
 def _check_gemm(qa, sa, a_block_rows, qb, sb):

@@ -211,6 +211,91 @@ int orc_quantize_global(const float *x, int64_t rows, int64_t cols, uint8_t *q, 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Power-of-two (UE8M0) block scales ("DeepGEMM: GPU high-efficiency BLAS    */
+/* kernel library", s3.1: the newer architecture takes its scaling factors  */
+/* as UE8M0, four packed into one 32-bit integer).  The pages do not say     */
+/* how the power of two is chosen; the reading taken here keeps the FP32     */
+/* recipe's guarantee that no element exceeds 448 after scaling: with        */
+/* t = binary32(amax / 448) as before, s = 2^e with e the smallest integer   */
+/* such that 2^e >= t, i.e. t rounded up to a power of two.  UE8M0 stores    */
+/* E = e + 127 in one byte, 0..254 (255 is NaN); e below -127 (t == 0 or     */
+/* t < 2^-127) is stored as E = 0.  Codes are RNE_E4M3(binary32(x / s)).     */
+/* ------------------------------------------------------------------------ */
+
+/* Smallest E in [0, 254] with 2^(E - 127) >= t, for finite t >= 0. */
+static int ue8m0_exponent(float t)
+{
+    int ex, e;
+    float f;
+    if (t == 0.0f)
+        return 0;
+    f = frexpf(t, &ex);                 /* t = f * 2^ex, f in [0.5, 1) */
+    e = (f == 0.5f) ? ex - 1 : ex;      /* ceil(log2 t) */
+    e += 127;
+    if (e < 0)
+        e = 0;
+    if (e > 254)
+        e = 254;
+    return e;
+}
+
+int orc_quantize_block_ue8m0(const float *x, int64_t rows, int64_t cols, int block_rows,
+                             uint8_t *q, uint8_t *exps)
+{
+    int64_t n_rb, n_kb, rb, kb, r, k;
+    if (!x || !q || !exps || rows < 0 || cols < 0)
+        return -1;
+    if (block_rows != 1 && block_rows != 128)
+        return -1;
+    for (r = 0; r < rows * cols; ++r)
+        if (!isfinite(x[r]))
+            return -1;
+    n_rb = ceil_div(rows, block_rows);
+    n_kb = ceil_div(cols, 128);
+    for (rb = 0; rb < n_rb; ++rb) {
+        int64_t r0 = rb * block_rows;
+        int64_t r1 = r0 + block_rows < rows ? r0 + block_rows : rows;
+        for (kb = 0; kb < n_kb; ++kb) {
+            int64_t k0 = kb * 128;
+            int64_t k1 = k0 + 128 < cols ? k0 + 128 : cols;
+            float amax = 0.0f, s;
+            int e;
+            for (r = r0; r < r1; ++r)
+                for (k = k0; k < k1; ++k) {
+                    float a = fabsf(x[r * cols + k]);
+                    if (a > amax)
+                        amax = a;
+                }
+            e = ue8m0_exponent(amax / 448.0f);
+            exps[kb * n_rb + rb] = (uint8_t)e;
+            s = ldexpf(1.0f, e - 127);          /* exact, 2^-127 .. 2^127 */
+            for (r = r0; r < r1; ++r)
+                for (k = k0; k < k1; ++k)
+                    q[r * cols + k] = orc_e4m3_encode_arith(x[r * cols + k] / s);
+        }
+    }
+    return 0;
+}
+
+/* Four exponents per 32-bit word along the K-block index: word
+ * [kb / 4][rb] holds the exponent of K block kb in byte kb % 4 (least
+ * significant byte first); bytes past the last K block are 0. */
+void orc_ue8m0_pack(const uint8_t *exps, int64_t n_kb, int64_t n_rb, uint32_t *packed)
+{
+    int64_t w, rb, j;
+    for (w = 0; w < ceil_div(n_kb, 4); ++w)
+        for (rb = 0; rb < n_rb; ++rb) {
+            uint32_t v = 0;
+            for (j = 0; j < 4; ++j) {
+                int64_t kb = 4 * w + j;
+                if (kb < n_kb)
+                    v |= (uint32_t)exps[kb * n_rb + rb] << (8 * j);
+            }
+            packed[w * n_rb + rb] = v;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantised NT GEMM ("... s2.2", "... s3.2"; NT layout from "DeepGEMM:   */
 /* GPU high-efficiency BLAS kernel library", s3.1 and s4.1).                 */
 /* Within one 128-wide K block every product dec(a)*dec(b) is a multiple of  */

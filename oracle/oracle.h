@@ -19,7 +19,8 @@
  *     s4.3  validate against an FP64 computation on the CPU
  *     s5.4  all-zero blocks need special handling (scale 0)
  *   "DeepGEMM: GPU high-efficiency BLAS kernel library" (pzsr.cn/news/21800):
- *     s3.1  NT layout (A not transposed, B transposed); SM90 FP32 scales
+ *     s3.1  NT layout (A not transposed, B transposed); SM90 FP32 scales;
+ *           SM100 UE8M0 scales, four packed per 32-bit integer
  *     s3.2, s3.3  grouped GEMM along M for MoE, contiguous layout with an
  *           M alignment per group
  *     s4.1  to_fp8(a) -> (a_fp8, a_sf); fp8_gemm_nt(c, a, b, a_sf, b_sf)
@@ -55,6 +56,16 @@ void orc_e4m3_decode_n(const uint8_t *codes, double *out, int64_t n);
  * (K-block-major).  Returns 0, or -1 on a bad argument / non-finite input. */
 int orc_quantize_block(const float *x, int64_t rows, int64_t cols, int block_rows,
                        uint8_t *q, float *scales);
+
+/* Block quantiser with power-of-two (UE8M0) scales: blocks as above;
+ * exps: uint8 [ceil(cols/128)][ceil(rows/block_rows)], E with scale
+ * 2^(E - 127) = t rounded up to a power of two, t = binary32(amax / 448)
+ * (E = 0 when t < 2^-127, including all-zero blocks); q = RNE_E4M3(x / s). */
+int orc_quantize_block_ue8m0(const float *x, int64_t rows, int64_t cols, int block_rows,
+                             uint8_t *q, uint8_t *exps);
+/* Pack exponents [n_kb][n_rb] four per word along K blocks:
+ * packed [ceil(n_kb/4)][n_rb], byte kb % 4 of word [kb/4][rb]; unused bytes 0. */
+void orc_ue8m0_pack(const uint8_t *exps, int64_t n_kb, int64_t n_rb, uint32_t *packed);
 
 /* Per-tensor scaling (the baseline the block method is compared with): one
  * FP32 scale = amax(x) / 448 for the whole tensor, then the same division and
