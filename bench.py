@@ -21,7 +21,8 @@ weights rotated over > 768 MB of copies so the 256 MB Infinity Cache cannot
 hold them), --config moe (8 experts, 1024 tokens top-2, up and down
 projections), --config small (128x256x512), --config outlier (8192^3 with
 heavy-tailed, hot-channel activations and 1x128 activation scales),
---config copy (a plain device copy of known size, used to calibrate the
+--config ue8m0 (the dense shapes with power-of-two block scales applied by the
+scaled matrix instruction), --config copy (a plain device copy of known size, used to calibrate the
 FETCH_SIZE/WRITE_SIZE counters), --config peak (the FP8 MFMA-loop probe: the
 matrix-core rate and shader clock this GPU sustains; the dense line also
 carries it as roofline.measured_peak).
@@ -165,11 +166,14 @@ class Timer:
 class Dense:
     rot = 1
 
-    def __init__(self, dg, shapes, seed=0, outlier=False):
+    def __init__(self, dg, shapes, seed=0, outlier=False, ue8m0=False):
         """outlier: A = heavy-tailed rows with 1% hot channels x100, quantised
-        with 1x128 (per-row) scales; otherwise A ~ N(0,1) with 128x128 scales."""
+        with 1x128 (per-row) scales; otherwise A ~ N(0,1) with 128x128 scales.
+        ue8m0: power-of-two scales packed four K blocks per int32, applied by
+        the scaled MFMA."""
         self.dg = dg
         self.outlier = outlier
+        self.ue8m0 = ue8m0
         self.a_br = 1 if outlier else 128
         self.items = []
         for (M, N, K) in shapes:
@@ -179,23 +183,38 @@ class Dense:
                 a_np = datagen.normal((M, K), 1.0, seed=seed, stream=0)
             a = torch.from_numpy(a_np).cuda()
             b = torch.from_numpy(datagen.normal((N, K), 0.02, seed=seed, stream=1)).cuda()
+            if ue8m0:
+                sa = torch.empty((cdiv(K // 128, 4), cdiv(M, self.a_br)), dtype=torch.int32,
+                                 device="cuda")
+                sb = torch.empty((cdiv(K // 128, 4), cdiv(N, 128)), dtype=torch.int32, device="cuda")
+            else:
+                sa = torch.empty((K // 128, cdiv(M, self.a_br)), dtype=torch.float32, device="cuda")
+                sb = torch.empty((K // 128, cdiv(N, 128)), dtype=torch.float32, device="cuda")
             self.items.append(dict(
-                M=M, N=N, K=K, a=a, b=b,
+                M=M, N=N, K=K, a=a, b=b, sa=sa, sb=sb,
                 qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
                 qb=torch.empty((N, K), dtype=torch.uint8, device="cuda"),
-                sa=torch.empty((K // 128, cdiv(M, self.a_br)), dtype=torch.float32, device="cuda"),
-                sb=torch.empty((K // 128, cdiv(N, 128)), dtype=torch.float32, device="cuda"),
                 c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         self.flops = sum(2.0 * it["M"] * it["N"] * it["K"] for it in self.items)
 
     def quant_a(self, it):
-        self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], self.a_br)
+        if self.ue8m0:
+            self.dg.dg_quantize_fp8_block_ue8m0(it["qa"], it["sa"], it["a"], self.a_br)
+        else:
+            self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], self.a_br)
 
     def quant_b(self, it):
-        self.dg.dg_quantize_fp8_block(it["qb"], it["sb"], it["b"], 128)
+        if self.ue8m0:
+            self.dg.dg_quantize_fp8_block_ue8m0(it["qb"], it["sb"], it["b"], 128)
+        else:
+            self.dg.dg_quantize_fp8_block(it["qb"], it["sb"], it["b"], 128)
 
     def gemm(self, it):
-        self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], self.a_br)
+        if self.ue8m0:
+            self.dg.dg_fp8_gemm_nt_ue8m0(it["c"], it["qa"], it["qb"], it["sa"], it["sb"],
+                                         self.a_br)
+        else:
+            self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], self.a_br)
 
     def step(self, i=0):
         for it in self.items:
@@ -214,6 +233,13 @@ class Dense:
                     "a_scales": "1x128", "b_scales": "128x128",
                     "step": "quantise A + quantise B + GEMM",
                     "inputs": "B ~ N(0,0.02^2), float32, seed 0"}
+        if self.ue8m0:
+            return {"workload": "dense LLM projection GEMMs, E4M3 128x128 blocks with "
+                                "power-of-two (UE8M0) scales packed 4 per int32, BF16 out",
+                    "shapes_mnk": [[it["M"], it["N"], it["K"]] for it in self.items],
+                    "a_scales": "128x128 UE8M0", "b_scales": "128x128 UE8M0",
+                    "step": "quantise A + quantise B + GEMM, per shape",
+                    "inputs": "A ~ N(0,1), B ~ N(0,0.02^2), float32, seed 0"}
         return {"workload": "dense LLM projection GEMMs, E4M3 128x128 block scales, BF16 out",
                 "shapes_mnk": [[it["M"], it["N"], it["K"]] for it in self.items],
                 "a_scales": "128x128", "b_scales": "128x128",
@@ -227,8 +253,9 @@ class Dense:
             tq_a = timer.time(lambda: self.quant_a(it), reps, key=("qa", n), calls=10)
             tq_b = timer.time(lambda: self.quant_b(it), reps, key=("qb", n), calls=10)
             tg = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
-            qbytes_a = M * K * 5 + 4 * (K // 128) * cdiv(M, self.a_br)
-            qbytes_b = N * K * 5 + 4 * (K // 128) * cdiv(N, 128)
+            sbytes = 1 if self.ue8m0 else 4
+            qbytes_a = M * K * 5 + sbytes * (K // 128) * cdiv(M, self.a_br)
+            qbytes_b = N * K * 5 + sbytes * (K // 128) * cdiv(N, 128)
             out.append({"mnk": [M, N, K],
                         "gemm_us": tg * 1e3, "gemm_tflops": 2.0 * M * N * K / (tg * 1e-3) / 1e12,
                         "quant_a_us": tq_a * 1e3, "quant_a_gbs": qbytes_a / (tq_a * 1e-3) / 1e9,
@@ -246,7 +273,8 @@ class Dense:
             t = timer.time(lambda: self.gemm(it), reps, key=("g", n), calls=4)
         flop = 2.0 * it["M"] * it["N"] * it["K"]
         ach = flop / (t * 1e-3) / 1e12
-        key = "gemm_tiled_kernel<256,%d,false> %dx%dx%d" % (self.a_br, it["M"], it["N"], it["K"])
+        key = "gemm_tiled_kernel<256,%d,false%s> %dx%dx%d" % (
+            self.a_br, ",true" if self.ue8m0 else "", it["M"], it["N"], it["K"])
         return {"kernel": key, "bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_FP8_TFLOPS,
                 "traffic": recorded_traffic(key, GEMM_TILED_SOURCES),
@@ -261,6 +289,8 @@ class Dense:
         128-row block of A, and compute 8 full output rows per thread.
         Extrapolated to the whole step on the same threads (B quantised once,
         A in M/128 blocks, M output rows)."""
+        if self.ue8m0:
+            return None
         import concurrent.futures as cf
         import oracle
         threads = max(1, min(16, os.cpu_count() or 1))
@@ -568,7 +598,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="dense",
-                    choices=["dense", "decode", "moe", "small", "outlier", "copy", "peak"])
+                    choices=["dense", "decode", "moe", "small", "outlier", "ue8m0", "copy",
+                             "peak"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -600,6 +631,8 @@ def main():
         w = Dense(dg, [(128, 256, 512)])
     elif args.config == "outlier":
         w = Dense(dg, [(8192, 8192, 8192)], outlier=True)
+    elif args.config == "ue8m0":
+        w = Dense(dg, DENSE, ue8m0=True)
     elif args.config == "decode":
         w = Decode(dg)
     else:

@@ -51,6 +51,10 @@ def _load():
     lib.dg_fp8_gemm_nt_workspace_bytes.argtypes = [i64, i64, i64]
     lib.dg_fp8_gemm_nt.restype = i32
     lib.dg_fp8_gemm_nt.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.dg_quantize_fp8_block_ue8m0.restype = i32
+    lib.dg_quantize_fp8_block_ue8m0.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    lib.dg_fp8_gemm_nt_ue8m0.restype = i32
+    lib.dg_fp8_gemm_nt_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     lib.dg_fp8_gemm_nt_fused_a.restype = i32
     lib.dg_fp8_gemm_nt_fused_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t,
                                            vp]
@@ -170,6 +174,42 @@ def dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows: int = 128, workspace=None,
            "dg_fp8_gemm_nt")
 
 
+def dg_quantize_fp8_block_ue8m0(q, sf, x, block_rows: int = 128, stream=None) -> None:
+    """x float32 [rows, cols] -> q (uint8/float8_e4m3fn [rows, cols]),
+    sf int32 [ceil(cols/512), ceil(rows/block_rows)] (UE8M0 exponents, four K
+    blocks per word)."""
+    _require(x, torch.float32, "x")
+    q = _codes(q, "q")
+    _require(sf, torch.int32, "sf")
+    rows, cols = x.shape
+    if q.shape != x.shape:
+        raise ValueError("q must have the shape of x")
+    if sf.numel() != cdiv(cdiv(cols, 128), 4) * cdiv(rows, block_rows):
+        raise ValueError("sf must hold ceil(cols/512)*ceil(rows/block_rows) int32")
+    _check(lib.dg_quantize_fp8_block_ue8m0(_ptr(q), _ptr(sf), _ptr(x), rows, cols, block_rows,
+                                           _stream(stream)), "dg_quantize_fp8_block_ue8m0")
+
+
+def dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, a_block_rows: int = 128, stream=None) -> None:
+    """C[M,N] (bf16) = A[M,K] . B[N,K]^T with packed UE8M0 block scales."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sfa, torch.int32, "sfa")
+    _require(sfb, torch.int32, "sfb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or c.shape != (M, N):
+        raise ValueError("shape mismatch: a %s, b %s, c %s" % (tuple(a.shape), tuple(b.shape),
+                                                              tuple(c.shape)))
+    if sfa.numel() != cdiv(cdiv(K, 128), 4) * cdiv(M, a_block_rows):
+        raise ValueError("sfa must hold ceil(K/512)*ceil(M/a_block_rows) int32")
+    if sfb.numel() != cdiv(cdiv(K, 128), 4) * cdiv(N, 128):
+        raise ValueError("sfb must hold ceil(K/512)*ceil(N/128) int32")
+    _check(lib.dg_fp8_gemm_nt_ue8m0(_ptr(c), _ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), a_block_rows,
+                                    M, N, K, _stream(stream)), "dg_fp8_gemm_nt_ue8m0")
+
+
 FUSED_A_MAX_M = 16
 
 
@@ -231,6 +271,17 @@ def to_fp8(x, block_rows: int = 128):
     return q, s
 
 
+def to_fp8_ue8m0(x, block_rows: int = 128):
+    """Quantise with power-of-two scales -> (codes uint8 [R, C], packed UE8M0
+    exponents int32 [ceil(C/512), ceil(R/block_rows)])."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    sf = torch.empty((cdiv(cdiv(cols, 128), 4), cdiv(rows, block_rows)), dtype=torch.int32,
+                     device=x.device)
+    dg_quantize_fp8_block_ue8m0(q, sf, x, block_rows)
+    return q, sf
+
+
 def fp8_gemm_nt(c, a, b, sa, sb, a_block_rows: int = 128, workspace=None):
     dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, workspace)
     return c
@@ -244,5 +295,6 @@ def fp8_grouped_gemm_contig(c, a, b, sa, sb, m_indices, a_block_rows: int = 1):
 __all__ = [
     "lib", "LIB_PATH", "DGError", "status_string", "get_mk_alignment_for_contiguous_layout",
     "dg_quantize_fp8_block", "dg_fp8_gemm_nt_workspace_bytes", "dg_fp8_gemm_nt",
-    "dg_fp8_gemm_nt_fused_a", "FUSED_A_MAX_M", "dg_fp8_grouped_gemm_contig", "to_fp8", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
+    "dg_fp8_gemm_nt_fused_a", "FUSED_A_MAX_M", "dg_fp8_grouped_gemm_contig", "to_fp8",
+    "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "to_fp8_ue8m0", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
 ]

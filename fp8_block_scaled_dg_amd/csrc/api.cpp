@@ -81,6 +81,20 @@ int dg_quantize_fp8_block(uint8_t* q, float* scales, const float* x, int64_t row
                                       static_cast<hipStream_t>(stream)));
 }
 
+int dg_quantize_fp8_block_ue8m0(uint8_t* q, int32_t* sf, const float* x, int64_t rows,
+                                int64_t cols, int block_rows, void* stream) {
+  if (!q || !sf || !x) return DG_ERR_NULL;
+  if (block_rows != 1 && block_rows != 128) return DG_ERR_UNSUPPORTED;
+  if (rows < 1 || cols < 1 || cols % 16 != 0) return DG_ERR_SHAPE;
+  const int64_t n_kb = (cols + 127) / 128;
+  const int64_t grid_y = block_rows == 128 ? (rows + 127) / 128 : (rows + 31) / 32;
+  if (grid_y > kMaxGridY || n_kb > INT32_MAX) return DG_ERR_SHAPE;
+  if (rows > INT64_MAX / cols) return DG_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(sf, 4)) return DG_ERR_ALIGN;
+  return from_hip(dg::launch_quantize_ue8m0(q, reinterpret_cast<uint32_t*>(sf), x, rows, cols,
+                                            block_rows, static_cast<hipStream_t>(stream)));
+}
+
 size_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return 0;
   return dg::skinny_applies(M, N, K) ? dg::skinny_workspace_bytes(M, N, K) : 0;
@@ -103,6 +117,22 @@ int dg_fp8_gemm_nt(uint16_t* c, const uint8_t* a, const uint8_t* b, const float*
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles > INT32_MAX) return DG_ERR_SHAPE;
   return from_hip(dg::launch_gemm_tiled(p, false, s));
+}
+
+int dg_fp8_gemm_nt_ue8m0(uint16_t* c, const uint8_t* a, const uint8_t* b, const int32_t* sfa,
+                         const int32_t* sfb, int a_block_rows, int64_t M, int64_t N, int64_t K,
+                         void* stream) {
+  // the FP32-scale checks apply unchanged (the scale pointers only need
+  // 4-byte alignment in both forms)
+  int st = check_gemm(c, a, b, reinterpret_cast<const float*>(sfa),
+                      reinterpret_cast<const float*>(sfb), a_block_rows, M, N, K);
+  if (st != DG_OK) return st;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles > INT32_MAX) return DG_ERR_SHAPE;
+  dg::GemmProblem p{c, a, b, nullptr, nullptr, nullptr, 1, a_block_rows, M, N, K};
+  p.sfa = reinterpret_cast<const uint32_t*>(sfa);
+  p.sfb = reinterpret_cast<const uint32_t*>(sfb);
+  return from_hip(dg::launch_gemm_tiled_ue8m0(p, static_cast<hipStream_t>(stream)));
 }
 
 int dg_fp8_gemm_nt_fused_a(uint16_t* c, const float* a, const uint8_t* b, const float* sb,

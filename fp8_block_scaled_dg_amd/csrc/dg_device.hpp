@@ -96,6 +96,38 @@ __device__ __forceinline__ uint32_t encode4_block(float4 v, const BlockScale& b)
   return (uint32_t)p | zero_codes4(v);
 }
 
+// ---- power-of-two (UE8M0) block scales (DeepGEMM page on pzsr.cn, s3.1:
+// UE8M0 scaling factors, four per 32-bit word) ----
+
+// Smallest E in [0, 254] with 2^(E - 127) >= t (t >= 0 finite): t rounded up
+// to a power of two, as a UE8M0 byte.  Subnormal t = m 2^-149 needs E = 1
+// only when m > 2^22 (t > 2^-127); t = 0 gives 0.
+__device__ __forceinline__ int ue8m0_exponent(float t) {
+  const uint32_t u = __float_as_uint(t);
+  const int ex = (int)(u >> 23);
+  const uint32_t m = u & 0x7FFFFFu;
+  if (ex == 0) return m > 0x400000u ? 1 : 0;
+  const int e = ex + (m != 0u ? 1 : 0);
+  return e > 254 ? 254 : e;
+}
+
+// 2^n as binary32 for n in [-127, 127] (2^-127 is subnormal).
+__device__ __forceinline__ float pow2f(int n) {
+  return n >= -126 ? __uint_as_float((uint32_t)(n + 127) << 23) : __uint_as_float(0x00400000u);
+}
+
+// Encoder parameters for the scale 2^(E - 127): the quotient x / s is the
+// exact product x * 2^(127 - E) (rounded only when it falls below binary32's
+// normal range, far under the smallest E4M3 subnormal), so no rescaling.
+__device__ __forceinline__ BlockScale pow2_block_scale(int e) {
+  BlockScale b;
+  b.s = pow2f(e - 127);
+  b.k = 1.0f;
+  b.sk = b.s;
+  b.r = pow2f(127 - e);
+  return b;
+}
+
 __device__ __forceinline__ float abs_max4(float m, float4 v) {
   return fmaxf(fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
 }

@@ -10,6 +10,10 @@ namespace dg {
 
 hipError_t launch_quantize(uint8_t* q, float* scales, const float* x, int64_t rows,
                            int64_t cols, int block_rows, hipStream_t stream);
+// Power-of-two (UE8M0) scales, packed four K blocks per word:
+// sf [ceil(cols/512)][ceil(rows/block_rows)].
+hipError_t launch_quantize_ue8m0(uint8_t* q, uint32_t* sf, const float* x, int64_t rows,
+                                 int64_t cols, int block_rows, hipStream_t stream);
 
 struct GemmProblem {
   uint16_t* c;
@@ -21,10 +25,16 @@ struct GemmProblem {
   int num_groups;            // grouped only, else 1
   int a_block_rows;          // 1 or 128
   int64_t M, N, K;
+  // power-of-two (UE8M0) scales, packed four K blocks per word, in place of
+  // sa / sb (dense tiled kernel only), else nullptr
+  const uint32_t* sfa = nullptr;
+  const uint32_t* sfb = nullptr;
 };
 
 // Large-tile MFMA kernel (dense or grouped).
 hipError_t launch_gemm_tiled(const GemmProblem& p, bool grouped, hipStream_t stream);
+// Dense 256 x 256 tile kernel with UE8M0 scales applied by the scaled MFMA.
+hipError_t launch_gemm_tiled_ue8m0(const GemmProblem& p, hipStream_t stream);
 
 // Skinny (small-M) kernel: workspace may be null (then no split-K).
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);

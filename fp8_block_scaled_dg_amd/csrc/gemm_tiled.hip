@@ -53,6 +53,8 @@ struct TiledArgs {
   const uint8_t* b;
   const float* sa;
   const float* sb;
+  const uint32_t* sfa;  // UE8M0 variant: packed exponent words instead of sa / sb
+  const uint32_t* sfb;
   const int32_t* m_indices;
   int num_groups;
   int M, N, K;
@@ -191,7 +193,12 @@ __device__ __forceinline__ bool grouped_tile(const TiledArgs& p, int blk, int n0
   return true;
 }
 
-template <int BM, int A_BLK, bool GROUPED>
+// E8: power-of-two (UE8M0) scales (DeepGEMM page on pzsr.cn, s3.1), four K
+// blocks per 32-bit word.  The scaled MFMA applies them itself -- each lane
+// passes the exponent byte of the row it feeds (one byte per 32 products of
+// that row; a 128-K block uses the same byte for all four) -- so the
+// accumulators chain through K with no partials and no promotion FMAs.
+template <int BM, int A_BLK, bool GROUPED, bool E8 = false>
 __global__ void __launch_bounds__(BM * BN / 128)
 gemm_tiled_kernel(TiledArgs p) {
   constexpr int WM = BM / 64;
@@ -251,9 +258,16 @@ gemm_tiled_kernel(TiledArgs p) {
 
   float sa_cur[4], sa_nxt[4];
   float sb_cur, sb_nxt;
+  int ea_cur[4], ea_nxt[4], eb_cur = 0, eb_nxt = 0;  // E8: exponent bytes (bits 7:0)
+  if constexpr (E8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sa_cur[i] = p.sa[sa_idx[i]];
-  sb_cur = sbbase[nb];
+    for (int i = 0; i < 4; ++i) ea_cur[i] = (int)(p.sfa[sa_idx[i]] & 0xFFu);
+    eb_cur = (int)(p.sfb[nb] & 0xFFu);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa_cur[i] = p.sa[sa_idx[i]];
+    sb_cur = sbbase[nb];
+  }
 
   lda.issue(p.a, lds0, wave, 0);
   ldb.issue(bbase, lds0 + A_BYTES, wave, 0);
@@ -266,12 +280,20 @@ gemm_tiled_kernel(TiledArgs p) {
     // The last step re-stages the final K slice into the idle buffer so the
     // body stays one basic block (the scheduling hints below need that).
     const int kn = kb + 1 < p.nkb ? kb + 1 : kb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sa_nxt[i] = p.sa[(int64_t)kn * p.sa_stride + sa_idx[i]];
-    sb_nxt = sbbase[(int64_t)kn * p.sb_stride + nb];
     float s[4];
+    if constexpr (E8) {
+      const int w = kn >> 2, sh = 8 * (kn & 3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = sa_cur[i] * sb_cur;
+      for (int i = 0; i < 4; ++i)
+        ea_nxt[i] = (int)((p.sfa[(int64_t)w * p.sa_stride + sa_idx[i]] >> sh) & 0xFFu);
+      eb_nxt = (int)((p.sfb[(int64_t)w * p.sb_stride + nb] >> sh) & 0xFFu);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa_nxt[i] = p.sa[(int64_t)kn * p.sa_stride + sa_idx[i]];
+      sb_nxt = sbbase[(int64_t)kn * p.sb_stride + nb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = sa_cur[i] * sb_cur;
+    }
 
     v8i af[4];
 #pragma unroll
@@ -293,8 +315,12 @@ gemm_tiled_kernel(TiledArgs p) {
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
       const int j = t >> 2, i = t & 3;
-      part[t & 1] =
-          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], zero, 0, 0, 0, 0, 0, 0);
+      if constexpr (E8)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bf[j & 1], af[i], acc[i][j], 0, 0, 0, eb_cur, 0, ea_cur[i]);
+      else
+        part[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], zero, 0,
+                                                                       0, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if ((t & 1) == 0 && (t >> 1) < IA + IB) {
         const int q = t >> 1;
@@ -308,18 +334,22 @@ gemm_tiled_kernel(TiledArgs p) {
         bf[(j + 1) & 1] = read_frag(cur + A_BYTES, wn * 128 + 16 * (j + 1), off0, off1);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (t > 0) {
+      if (!E8 && t > 0) {
         const int tp = t - 1, jp = tp >> 2, ip = tp & 3;
         acc[ip][jp] += part[tp & 1] * s[ip];
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    acc[3][7] += part[1] * s[3];
+    if constexpr (E8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa_cur[i] = sa_nxt[i];
+      for (int i = 0; i < 4; ++i) ea_cur[i] = ea_nxt[i];
+      eb_cur = eb_nxt;
+    } else {
+      acc[3][7] += part[1] * s[3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa_cur[i] = sa_nxt[i];
+      sb_cur = sb_nxt;
     }
-    sb_cur = sb_nxt;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
@@ -532,10 +562,12 @@ gemm_ring_kernel(TiledArgs p) {
   }
 }
 
-template <bool RING, int A_BLK, bool GROUPED>
+template <bool RING, int A_BLK, bool GROUPED, bool E8 = false>
 hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
+  static_assert(!(E8 && (RING || GROUPED)), "UE8M0 scales: dense two-stage kernel only");
   TiledArgs p;
   p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.sfa = q.sfa; p.sfb = q.sfb;
   p.m_indices = q.m_indices; p.num_groups = q.num_groups;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
   p.nkb = (int)(q.K / BK);
@@ -548,8 +580,8 @@ hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   if (RING)
     hipLaunchKernelGGL((gemm_ring_kernel<A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<256, A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream,
-                       p);
+    hipLaunchKernelGGL((gemm_tiled_kernel<256, A_BLK, GROUPED, E8>), dim3(grid), dim3(512), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
@@ -576,6 +608,11 @@ hipError_t launch_gemm_tiled(const GemmProblem& q, bool grouped, hipStream_t str
                                : launch_one<true, 128, false>(q, stream);
   return q.a_block_rows == 1 ? launch_one<false, 1, false>(q, stream)
                              : launch_one<false, 128, false>(q, stream);
+}
+
+hipError_t launch_gemm_tiled_ue8m0(const GemmProblem& q, hipStream_t stream) {
+  return q.a_block_rows == 1 ? launch_one<false, 1, false, true>(q, stream)
+                             : launch_one<false, 128, false, true>(q, stream);
 }
 
 }  // namespace dg

@@ -73,6 +73,23 @@ int dg_quantize_fp8_block(uint8_t *q, float *scales, const float *x,
                           int64_t rows, int64_t cols, int block_rows, void *stream);
 
 /*
+ * Block quantiser with power-of-two (UE8M0) scales [D s3.1: the newer
+ * architecture's scaling factors are UE8M0, four packed into one 32-bit
+ * integer; Q s4.2 for the rest of the recipe].
+ *   x, q, block_rows, requirements: as dg_quantize_fp8_block.
+ *   sf : out, int32 [ceil(cols/512)][ceil(rows/block_rows)], 4-byte aligned:
+ *        byte kb % 4 (least significant first) of word [kb / 4][rb] holds
+ *        E for block (rb, kb); bytes past the last K block are written as 0.
+ * For each block: t = amax / 448 (binary32 division, as in the FP32 recipe);
+ * the scale is 2^(E - 127) with E the smallest value in [0, 254] such that
+ * 2^(E - 127) >= t (t rounded up to a power of two, so no element exceeds
+ * 448 after scaling; E = 0 for t < 2^-127, all-zero blocks included); then
+ * q = round-to-nearest-even-E4M3(binary32(x / 2^(E - 127))), sign kept.
+ */
+int dg_quantize_fp8_block_ue8m0(uint8_t *q, int32_t *sf, const float *x,
+                                int64_t rows, int64_t cols, int block_rows, void *stream);
+
+/*
  * Workspace bytes dg_fp8_gemm_nt can use for split-K on this shape (0 when
  * the chosen plan needs none).  Passing a smaller, non-NULL workspace is an
  * error; passing NULL/0 selects a plan that needs none.
@@ -104,6 +121,22 @@ int dg_fp8_gemm_nt(uint16_t *c, const uint8_t *a, const uint8_t *b,
                    const float *sa, const float *sb, int a_block_rows,
                    int64_t M, int64_t N, int64_t K,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * NT GEMM with power-of-two (UE8M0) block scales [D s3.1; Q s2.2, s3.2]:
+ *   C[m][n] = bf16( sum_kb 2^(Ea(m,kb) + Eb(n,kb) - 254) * sum_{k in kb} A[m][k] * B[n][k] )
+ * with FP32 accumulation.  The scales are applied inside gfx950's scaled FP8
+ * matrix instruction, so the sum runs in one FP32 accumulator per output
+ * with no separate promotion step.
+ *   c, a, b, a_block_rows, M, N, K and their requirements: as dg_fp8_gemm_nt.
+ *   sfa : int32 [ceil(K/512)][ceil(M/a_block_rows)], packed as written by
+ *         dg_quantize_fp8_block_ue8m0; sfb : int32 [ceil(K/512)][ceil(N/128)].
+ * Every shape runs the 256 x 256 tile kernel (no small-M plan).
+ * Deterministic.
+ */
+int dg_fp8_gemm_nt_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                         const int32_t *sfa, const int32_t *sfb, int a_block_rows,
+                         int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
  * NT GEMM of FP32 activations with FP8 weights, the activations quantised

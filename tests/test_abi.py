@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for need in ("dg_quantize_fp8_block", "dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contig",
                  "dg_abi_version", "dg_status_string", "dg_fp8_gemm_nt_workspace_bytes",
-                 "dg_get_mk_alignment_for_contiguous_layout", "dg_fp8_gemm_nt_fused_a"):
+                 "dg_get_mk_alignment_for_contiguous_layout", "dg_fp8_gemm_nt_fused_a",
+                 "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0"):
         assert need in names
 
 
@@ -132,3 +133,20 @@ def test_fused_a_validation(dg):
     need = dg.dg_fp8_gemm_nt_workspace_bytes(16, 4096, 4096)
     assert gf(lib, M=16, N=4096, K=4096, ws=P, wsb=16) == 5
     assert gf(lib, M=16, N=4096, K=4096, ws=P1, wsb=need) == 4
+
+
+def test_ue8m0_validation(dg):
+    lib = dg.lib
+    assert lib.dg_quantize_fp8_block_ue8m0(None, P, P, 128, 128, 128, None) == 1
+    assert lib.dg_quantize_fp8_block_ue8m0(P, P, P, 128, 128, 64, None) == 3
+    assert lib.dg_quantize_fp8_block_ue8m0(P, P, P, 128, 24, 128, None) == 2
+    assert lib.dg_quantize_fp8_block_ue8m0(P, ctypes.c_void_p(0x10002), P, 128, 128, 128,
+                                           None) == 4
+
+    def ge(c=P, a=P, b=P, sfa=P, sfb=P, br=128, M=256, N=256, K=256):
+        return lib.dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, br, M, N, K, None)
+    for kw in ("c", "a", "b", "sfa", "sfb"):
+        assert ge(**{kw: None}) == 1
+    assert ge(br=2) == 3
+    assert ge(M=0) == 2 and ge(N=260) == 2 and ge(K=200) == 2
+    assert ge(a=P1) == 4 and ge(sfb=ctypes.c_void_p(0x10002)) == 4

@@ -1,0 +1,167 @@
+"""GPU parity of the power-of-two (UE8M0) scale path (pzsr.cn DeepGEMM page
+s3.1; the recipe otherwise as on the lpnh.cn FP8 block-quantised GEMM page
+s4.2): the quantiser's codes and packed exponent words must equal the
+oracle's bit for bit; the GEMM, which applies the scales inside gfx950's
+scaled FP8 matrix instruction, must meet the GEMM tolerance against the
+oracle's FP64 product of the same codes and scales."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dg():
+    need_gpu()
+    import fp8_block_scaled_dg_amd as m
+    return m
+
+
+def gpu_quant(dg, x, br):
+    q, sf = dg.to_fp8_ue8m0(dev(x), br)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), sf.cpu().numpy()
+
+
+def check_quant(dg, orc, x, br, what):
+    q, sf = gpu_quant(dg, x, br)
+    oq, oe = orc.quantize_ue8m0(x, br)
+    assert np.array_equal(q, oq), what
+    assert np.array_equal(sf, orc.pack_ue8m0(oe)), what
+
+
+@pytest.mark.parametrize("br", [128, 1])
+@pytest.mark.parametrize("rows,cols", [(128, 512), (256, 640), (1, 128), (3, 16), (200, 384),
+                                       (129, 1024), (300, 144), (64, 1664)])
+def test_quantize_ue8m0_small_and_ragged(dg, orc, rows, cols, br):
+    """Ragged rows and columns, K-block counts of 1 to 13 (partial last words)."""
+    x = datagen.normal((rows, cols), 1.0, seed=rows + cols, stream=br)
+    check_quant(dg, orc, x, br, "%dx%d/%d" % (rows, cols, br))
+
+
+@pytest.mark.parametrize("br", [128, 1])
+def test_quantize_ue8m0_special_blocks(dg, orc, br):
+    x = datagen.normal((256, 1024), 0.02, seed=3)
+    x[:128, :128] = 0.0
+    x[5, 7] = -0.0
+    x[:, 128:256] *= np.float32(1e-38)                   # t subnormal
+    x[:, 256:384] *= np.float32(1e-44)                   # t below 2^-127: E = 0
+    x[:, 384:512] = np.float32(2.0) ** np.arange(-20, 108, dtype=np.float32)[None, :]
+    x[:, 512:640] *= np.float32(1e30)
+    blk = x[:, 640:768]
+    blk /= np.abs(blk).max()
+    blk *= np.float32(448.0 * 2.0 ** -5)                 # t exactly a power of two
+    x[0, 768] = np.nextafter(np.float32(448.0), np.float32(np.inf))   # t one ulp above 1
+    x[3, 896:] = -np.abs(x[3, 896:])
+    check_quant(dg, orc, x, br, "special/%d" % br)
+
+
+@pytest.mark.parametrize("rows,cols,br", [(4096, 7168, 128), (64, 16384, 1), (2816, 11008, 1)])
+def test_quantize_ue8m0_full_size(dg, orc, rows, cols, br):
+    x = datagen.normal((rows, cols), 1.0 if br == 1 else 0.02, seed=0, stream=1)
+    check_quant(dg, orc, x, br, "%dx%d/%d" % (rows, cols, br))
+
+
+def operands(orc, M, N, K, br, seed=0):
+    a = datagen.normal((M, K), 1.0, seed=seed, stream=0)
+    b = datagen.normal((N, K), 0.02, seed=seed, stream=1)
+    qa, ea = orc.quantize_ue8m0(a, br)
+    qb, eb = orc.quantize_ue8m0(b, 128)
+    return qa, ea, qb, eb
+
+
+def run_gemm(dg, orc, qa, ea, qb, eb, br):
+    M, N = qa.shape[0], qb.shape[0]
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm_nt_ue8m0(c, dev(qa), dev(qb), dev(orc.pack_ue8m0(ea)),
+                            dev(orc.pack_ue8m0(eb)), br)
+    torch.cuda.synchronize()
+    return c
+
+
+@pytest.mark.parametrize("br", [128, 1])
+@pytest.mark.parametrize("M,N,K", [(128, 256, 512), (256, 256, 128), (512, 768, 384),
+                                   (300, 520, 1024), (200, 264, 640), (1, 256, 256),
+                                   (16, 512, 1664), (257, 136, 128)])
+def test_gemm_ue8m0_small_full_compare(dg, orc, M, N, K, br):
+    """Several tiles, ragged M and N, K-block counts that leave partial words."""
+    qa, ea, qb, eb = operands(orc, M, N, K, br, seed=M + N + K)
+    ref = orc.gemm_nt(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), a_block_rows=br)
+    c = bf16_to_f64(run_gemm(dg, orc, qa, ea, qb, eb, br))
+    assert_close(c, ref, what="ue8m0 %dx%dx%d/%d" % (M, N, K, br))
+
+
+def test_gemm_ue8m0_exact_on_integers(dg, orc):
+    """Codes for 0, +-1, +-2 with exponents that vary per row (A) and per
+    128-row block (B): every output is a small integer times a power of two
+    that BF16 holds exactly, so the result must be bit-exact.  Pins which
+    exponent byte applies to which row and column."""
+    g = np.random.default_rng(9)
+    codes = np.array([0x00, 0x38, 0xB8, 0x40, 0xC0], np.uint8)
+    M, N, K = 256, 512, 640
+    qa = codes[g.integers(0, 5, (M, K))]
+    qb = codes[g.integers(0, 5, (N, K))]
+    qa[:, 2:] = 0                # one K block with two products per output: |sum| <= 8,
+                                 # times one power of two -- exact in BF16
+    ea = g.integers(124, 131, (K // 128, M)).astype(np.uint8)
+    eb = g.integers(122, 133, (K // 128, N // 128)).astype(np.uint8)
+    ref = orc.gemm_nt(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), a_block_rows=1)
+    c = bf16_to_f64(run_gemm(dg, orc, qa, ea, qb, eb, 1))
+    assert np.array_equal(c, ref)
+
+
+def test_gemm_ue8m0_one_hot_exponents(dg, orc):
+    """All codes 1.0; one A row, one B row block and one K block at a time get
+    a larger exponent: exactly the outputs that block feeds must change."""
+    M, N, K = 256, 512, 512
+    qa = np.full((M, K), 0x38, np.uint8)
+    qb = np.full((N, K), 0x38, np.uint8)
+    base_a = np.full((K // 128, M), 127, np.uint8)
+    base_b = np.full((K // 128, N // 128), 127, np.uint8)
+    for (kb, m, nb) in [(0, 0, 0), (3, 200, 1), (1, 17, 3), (2, 255, 2)]:
+        ea = base_a.copy(); ea[kb, m] = 130
+        eb = base_b.copy(); eb[kb, nb] = 125
+        ref = orc.gemm_nt(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), a_block_rows=1)
+        c = bf16_to_f64(run_gemm(dg, orc, qa, ea, qb, eb, 1))
+        assert np.array_equal(c, ref), (kb, m, nb)
+
+
+def test_gemm_ue8m0_full_size_sampled(dg, orc):
+    M, N, K, br = 4096, 4096, 7168, 128
+    qa, ea, qb, eb = operands(orc, M, N, K, br)
+    c = run_gemm(dg, orc, qa, ea, qb, eb, br)
+    g = np.random.default_rng(1)
+    pm = np.concatenate([g.integers(0, M, 1500), np.full(N, M - 1), np.arange(0, M, 8)])
+    pn = np.concatenate([g.integers(0, N, 1500), np.arange(N), np.full(M // 8, N - 1)])
+    assert pm.max() < M and pn.max() < N
+    ref = orc.gemm_nt_points(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), pm, pn,
+                             a_block_rows=br)
+    got = c[torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()]
+    rms = float(np.sqrt(np.mean(ref[:1500] ** 2)))
+    assert_close(got.float().cpu().numpy().astype(np.float64), ref, rms=rms,
+                 what="ue8m0 %dx%dx%d" % (M, N, K))
+
+
+def test_end_to_end_ue8m0_and_determinism(dg, orc):
+    """GPU quantiser feeding the GPU GEMM, against the oracle on the same FP32
+    inputs; two runs give identical bits."""
+    M, N, K = 512, 768, 1024
+    a = datagen.normal((M, K), 1.0, seed=21, stream=0)
+    b = datagen.normal((N, K), 0.02, seed=21, stream=1)
+    qa, sfa = dg.to_fp8_ue8m0(dev(a), 1)
+    qb, sfb = dg.to_fp8_ue8m0(dev(b), 128)
+    outs = []
+    for _ in range(2):
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        dg.dg_fp8_gemm_nt_ue8m0(c, qa, qb, sfa, sfb, 1)
+        outs.append(c)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    oqa, oea = orc.quantize_ue8m0(a, 1)
+    oqb, oeb = orc.quantize_ue8m0(b, 128)
+    ref = orc.gemm_nt(oqa, orc.ue8m0_scales(oea), oqb, orc.ue8m0_scales(oeb), a_block_rows=1)
+    assert_close(bf16_to_f64(outs[0]), ref, what="ue8m0 end to end")
