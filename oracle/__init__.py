@@ -74,6 +74,9 @@ def _load():
     lib.orc_quantize_block_ue8m0.argtypes = [f32p, i64, i64, ctypes.c_int, u8p, u8p]
     lib.orc_ue8m0_pack.restype = None
     lib.orc_ue8m0_pack.argtypes = [u8p, i64, i64, ctypes.POINTER(ctypes.c_uint32)]
+    lib.orc_epilogue.restype = ctypes.c_int
+    lib.orc_epilogue.argtypes = [f64p, i64, i64, ctypes.c_int, ctypes.POINTER(ctypes.c_uint16),
+                                 f64p]
     lib.orc_quantize_global.restype = ctypes.c_int
     lib.orc_quantize_global.argtypes = [f32p, i64, i64, u8p, f32p]
     lib.orc_gemm_nt.restype = ctypes.c_int
@@ -254,3 +257,28 @@ def grouped_gemm_contig(qa, sa, qb, sb, m_indices, a_block_rows: int = 128,
     if rc != 0:
         raise ValueError("oracle grouped_gemm_contig rejected its input")
     return ref
+
+
+EPILOGUES = {"none": 0, "relu": 1, "silu": 2, "gelu": 3, "swiglu": 4}
+
+
+def epilogue(acc, act: str = "none", residual=None) -> np.ndarray:
+    """Epilogue on a float64 product [M, N] (bjdmk.com.cn DeepGEMM page s3.2;
+    SwiGLU per the pzsr.cn page s2.3): activation, or SwiGLU over interleaved
+    gate/up columns (output N/2 columns), then + residual (BF16 bits as uint16
+    [M, Nout]) if given.  Returns float64 [M, Nout]."""
+    a = _c(acc, np.float64)
+    M, N = a.shape
+    code = EPILOGUES[act]
+    n_out = N // 2 if code == 4 else N
+    out = np.empty((M, n_out), dtype=np.float64)
+    r = None
+    if residual is not None:
+        r = _c(residual, np.uint16)
+        assert r.shape == (M, n_out)
+    rc = _load().orc_epilogue(_ptr(a, ctypes.c_double), M, N, code,
+                              None if r is None else _ptr(r, ctypes.c_uint16),
+                              _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle epilogue rejected its input")
+    return out

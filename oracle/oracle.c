@@ -402,3 +402,56 @@ int orc_grouped_gemm_contig(const uint8_t *qa, const float *sa, int a_block_rows
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Epilogue fused into the GEMM's write-back ("省算力新利器 DeepGEMM",         */
+/* bjdmk.com.cn, s3.2: element-wise operators -- activations, residual add  */
+/* -- applied while the product is still on chip; "DeepGEMM: GPU high-      */
+/* efficiency BLAS kernel library", s2.3: SwiGLU inside the MoE kernel).    */
+/* Applied here in FP64 to the FP64 product:                                 */
+/*   none: v;  relu: max(v, 0);  silu: v / (1 + e^-v);                        */
+/*   gelu: v/2 (1 + erf(v / sqrt 2));                                         */
+/*   swiglu: with B rows interleaved (row 2j gate, row 2j+1 up), output      */
+/*     column j = silu(acc[2j]) * acc[2j+1], so the output has N/2 columns.  */
+/* Then, if given, the BF16 residual [M][Nout] is added.                     */
+/* ------------------------------------------------------------------------ */
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int orc_epilogue(const double *acc, int64_t M, int64_t N, int act, const uint16_t *residual,
+                 double *out)
+{
+    int64_t m, j, n_out;
+    if (!acc || !out || M < 0 || N < 0 || act < 0 || act > 4)
+        return -1;
+    if (act == 4 && N % 2 != 0)
+        return -1;
+    n_out = act == 4 ? N / 2 : N;
+    for (m = 0; m < M; ++m)
+        for (j = 0; j < n_out; ++j) {
+            double v;
+            if (act == 4) {
+                v = silu(acc[m * N + 2 * j]) * acc[m * N + 2 * j + 1];
+            } else {
+                double a = acc[m * N + j];
+                switch (act) {
+                case 1: v = a > 0.0 ? a : 0.0; break;
+                case 2: v = silu(a); break;
+                case 3: v = 0.5 * a * (1.0 + erf(a / sqrt(2.0))); break;
+                default: v = a; break;
+                }
+            }
+            if (residual)
+                v += bf16_value(residual[m * n_out + j]);
+            out[m * n_out + j] = v;
+        }
+    return 0;
+}

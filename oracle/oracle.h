@@ -97,6 +97,14 @@ int orc_grouped_gemm_contig(const uint8_t *qa, const float *sa, int a_block_rows
                             int64_t M, int64_t N, int64_t K,
                             int64_t rows_begin, int64_t rows_end, double *ref);
 
+/* Epilogue on an FP64 product acc [M][N] (bjdmk.com.cn page s3.2; pzsr.cn
+ * page s2.3 for SwiGLU): act 0 none, 1 relu, 2 silu, 3 gelu (erf form),
+ * 4 swiglu (B rows interleaved gate/up: out[m][j] = silu(acc[m][2j]) *
+ * acc[m][2j+1], N/2 columns); then + residual (BF16 bits [M][Nout]) if not
+ * NULL.  out: FP64 [M][Nout].  Returns 0, or -1 on a bad argument. */
+int orc_epilogue(const double *acc, int64_t M, int64_t N, int act, const uint16_t *residual,
+                 double *out);
+
 #ifdef __cplusplus
 }
 #endif
