@@ -22,7 +22,9 @@ hold them), --config moe (8 experts, 1024 tokens top-2, up and down
 projections), --config small (128x256x512), --config outlier (8192^3 with
 heavy-tailed, hot-channel activations and 1x128 activation scales),
 --config ue8m0 (the dense shapes with power-of-two block scales applied by the
-scaled matrix instruction), --config copy (a plain device copy of known size, used to calibrate the
+scaled matrix instruction), --config epilogue (SwiGLU and in-place residual
+fused into the write-back of MLP-shaped GEMMs, against the unfused pair),
+--config copy (a plain device copy of known size, used to calibrate the
 FETCH_SIZE/WRITE_SIZE counters), --config peak (the FP8 MFMA-loop probe: the
 matrix-core rate and shader clock this GPU sustains; the dense line also
 carries it as roofline.measured_peak).
@@ -434,6 +436,94 @@ class Decode:
         return None
 
 
+class Epilogue:
+    """Fused epilogues on LLM-MLP-shaped GEMMs (2048 tokens): the up
+    projection with gate and up interleaved and SwiGLU applied on write-back
+    (N = 2 x 11008, K = 4096, C has 11008 columns), and the down projection
+    with a BF16 residual added on write-back (N = 4096, K = 11008).  A step =
+    quantise A (1x128 scales) + the fused GEMM, per shape; B is quantised
+    once.  The breakdown also times the unfused pair (plain GEMM, then the
+    same element-wise step as a separate PyTorch operation) for comparison."""
+    rot = 1
+
+    def __init__(self, dg, seed=0):
+        self.dg = dg
+        self.items = []
+        for (M, N, K, act) in [(2048, 22016, 4096, "swiglu"), (2048, 4096, 11008, "none")]:
+            a = torch.from_numpy(datagen.normal((M, K), 1.0, seed=seed, stream=0)).cuda()
+            b = torch.from_numpy(datagen.normal((N, K), 0.02, seed=seed, stream=1)).cuda()
+            qb, sb = dg.to_fp8(b, 128)
+            n_out = N // 2 if act == "swiglu" else N
+            res = None
+            if act == "none":
+                res = torch.from_numpy(datagen.normal((M, N), 1.0, seed=seed, stream=2)).cuda()
+                res = res.to(torch.bfloat16)
+            self.items.append(dict(
+                M=M, N=N, K=K, act=act, a=a, qb=qb, sb=sb, res=res,
+                qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
+                sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
+                c=torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda"),
+                c_full=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+        self.flops = sum(2.0 * it["M"] * it["N"] * it["K"] for it in self.items)
+
+    def fused(self, it):
+        # the residual is read from its own buffer here (the same bytes as in
+        # place, without re-seeding C before every call)
+        self.dg.dg_fp8_gemm_nt_epilogue(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], 1,
+                                        act=it["act"], residual=it["res"])
+
+    def unfused(self, it):
+        self.dg.dg_fp8_gemm_nt(it["c_full"], it["qa"], it["qb"], it["sa"], it["sb"], 1)
+        if it["act"] == "swiglu":
+            g = it["c_full"][:, 0::2].float()
+            u = it["c_full"][:, 1::2].float()
+            it["c"].copy_(torch.nn.functional.silu(g) * u)
+        else:
+            torch.add(it["c_full"], it["res"], out=it["c"])
+
+    def step(self, i=0):
+        for it in self.items:
+            self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
+            self.fused(it)
+
+    def outputs(self):
+        return [t for it in self.items for t in (it["qa"], it["sa"], it["c"])]
+
+    def config(self):
+        return {"workload": "fused GEMM epilogues at 2048 tokens: up projection 4096 -> 2 x 11008 "
+                            "with interleaved gate/up and SwiGLU on write-back; down projection "
+                            "11008 -> 4096 with a BF16 residual added on write-back",
+                "shapes_mnk": [[it["M"], it["N"], it["K"]] for it in self.items],
+                "a_scales": "1x128", "b_scales": "128x128",
+                "step": "quantise A + fused GEMM per shape (B quantised once)",
+                "inputs": "A ~ N(0,1), B ~ N(0,0.02^2), residual ~ N(0,1) in BF16, seed 0"}
+
+    def breakdown(self, timer, reps):
+        out = []
+        for n, it in enumerate(self.items):
+            tf = timer.time(lambda: self.fused(it), reps, key=("ef", n), calls=4)
+            tu = timer.time(lambda: self.unfused(it), reps, key=("eu", n), calls=4)
+            out.append({"mnk": [it["M"], it["N"], it["K"]], "epilogue": it["act"] if it["res"] is None
+                        else "residual", "fused_us": tf * 1e3, "unfused_us": tu * 1e3,
+                        "fused_tflops": 2.0 * it["M"] * it["N"] * it["K"] / (tf * 1e-3) / 1e12})
+        return out
+
+    def roofline(self, timer, reps):
+        it = self.items[0]
+        st = timer.stats(lambda: self.fused(it), max(reps, 25), ("ef", 0), calls=4)
+        t = st["mean"] * 1e-3
+        flop = 2.0 * it["M"] * it["N"] * it["K"]
+        ach = flop / (t * 1e-3) / 1e12
+        return {"kernel": "gemm_tiled_kernel<256,1,false> %dx%dx%d + SwiGLU epilogue"
+                          % (it["M"], it["N"], it["K"]),
+                "bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_FP8_TFLOPS, "traffic": None, "avg_launch_us": t * 1e3,
+                "launch_us_stats": st}
+
+    def cpu_baseline(self):
+        return None
+
+
 class Moe:
     rot = 1
 
@@ -598,8 +688,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="dense",
-                    choices=["dense", "decode", "moe", "small", "outlier", "ue8m0", "copy",
-                             "peak"])
+                    choices=["dense", "decode", "moe", "small", "outlier", "ue8m0", "epilogue",
+                             "copy", "peak"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -633,6 +723,8 @@ def main():
         w = Dense(dg, [(8192, 8192, 8192)], outlier=True)
     elif args.config == "ue8m0":
         w = Dense(dg, DENSE, ue8m0=True)
+    elif args.config == "epilogue":
+        w = Epilogue(dg)
     elif args.config == "decode":
         w = Decode(dg)
     else:

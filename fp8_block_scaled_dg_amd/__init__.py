@@ -55,6 +55,9 @@ def _load():
     lib.dg_quantize_fp8_block_ue8m0.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     lib.dg_fp8_gemm_nt_ue8m0.restype = i32
     lib.dg_fp8_gemm_nt_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    lib.dg_fp8_gemm_nt_epilogue.restype = i32
+    lib.dg_fp8_gemm_nt_epilogue.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp, vp,
+                                            ctypes.c_size_t, vp]
     lib.dg_fp8_gemm_nt_fused_a.restype = i32
     lib.dg_fp8_gemm_nt_fused_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t,
                                            vp]
@@ -233,6 +236,40 @@ def dg_fp8_gemm_nt_fused_a(c, a, b, sb, workspace=None, stream=None) -> None:
            "dg_fp8_gemm_nt_fused_a")
 
 
+EPILOGUES = {"none": 0, "relu": 1, "silu": 2, "gelu": 3, "swiglu": 4}
+
+
+def dg_fp8_gemm_nt_epilogue(c, a, b, sa, sb, a_block_rows: int = 128, act: str = "none",
+                            residual=None, workspace=None, stream=None) -> None:
+    """C = epilogue(A . B^T): act in EPILOGUES (swiglu: B rows interleave gate
+    and up, C has N/2 columns), plus an optional BF16 residual [M, Nout]
+    (may be c itself)."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sa, torch.float32, "sa")
+    _require(sb, torch.float32, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    code = EPILOGUES[act]
+    n_out = N // 2 if code == EPILOGUES["swiglu"] else N
+    if b.shape[1] != K or c.shape != (M, n_out):
+        raise ValueError("shape mismatch: a %s, b %s, c %s (act %s)"
+                         % (tuple(a.shape), tuple(b.shape), tuple(c.shape), act))
+    if sa.numel() != cdiv(K, 128) * cdiv(M, a_block_rows):
+        raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
+    if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        if residual.shape != (M, n_out):
+            raise ValueError("residual must be [M, Nout]")
+    _check(lib.dg_fp8_gemm_nt_epilogue(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), a_block_rows,
+                                       M, N, K, code, _ptr(residual), _ptr(workspace),
+                                       _workspace_bytes(workspace), _stream(stream)),
+           "dg_fp8_gemm_nt_epilogue")
+
+
 def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices,
                                stream=None) -> None:
     """Grouped M-contiguous: a [M,K], b [G,N,K], sb [G,K/128,ceil(N/128)],
@@ -296,5 +333,6 @@ __all__ = [
     "lib", "LIB_PATH", "DGError", "status_string", "get_mk_alignment_for_contiguous_layout",
     "dg_quantize_fp8_block", "dg_fp8_gemm_nt_workspace_bytes", "dg_fp8_gemm_nt",
     "dg_fp8_gemm_nt_fused_a", "FUSED_A_MAX_M", "dg_fp8_grouped_gemm_contig", "to_fp8",
-    "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "to_fp8_ue8m0", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
+    "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "to_fp8_ue8m0",
+    "dg_fp8_gemm_nt_epilogue", "EPILOGUES", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
 ]

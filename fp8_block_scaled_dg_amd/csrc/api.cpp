@@ -57,7 +57,7 @@ const char* dg_status_string(int status) {
     case DG_OK: return "ok";
     case DG_ERR_NULL: return "a required pointer is NULL";
     case DG_ERR_SHAPE: return "invalid or unsupported shape";
-    case DG_ERR_UNSUPPORTED: return "unsupported block_rows or group count";
+    case DG_ERR_UNSUPPORTED: return "unsupported block_rows, group count or epilogue";
     case DG_ERR_ALIGN: return "pointer not suitably aligned";
     case DG_ERR_WORKSPACE: return "workspace smaller than required";
     case DG_ERR_HIP: return "HIP runtime error";
@@ -103,12 +103,24 @@ size_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 int dg_fp8_gemm_nt(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
                    const float* sb, int a_block_rows, int64_t M, int64_t N, int64_t K,
                    void* workspace, size_t workspace_bytes, void* stream) {
+  return dg_fp8_gemm_nt_epilogue(c, a, b, sa, sb, a_block_rows, M, N, K, DG_EPI_NONE, nullptr,
+                                 workspace, workspace_bytes, stream);
+}
+
+int dg_fp8_gemm_nt_epilogue(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
+                            const float* sb, int a_block_rows, int64_t M, int64_t N, int64_t K,
+                            int act, const uint16_t* residual, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
   if (st != DG_OK) return st;
+  if (act < DG_EPI_NONE || act > DG_EPI_SWIGLU) return DG_ERR_UNSUPPORTED;
+  if (residual && !aligned(residual, 16)) return DG_ERR_ALIGN;
   const bool skinny = dg::skinny_applies(M, N, K);
   st = check_workspace(M, N, K, &workspace, &workspace_bytes);
   if (st != DG_OK) return st;
   dg::GemmProblem p{c, a, b, sa, sb, nullptr, 1, a_block_rows, M, N, K};
+  p.epi.act = act;
+  p.epi.res = residual;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (skinny) {
     if (dg::stream_preferred(M, N, K)) return from_hip(dg::launch_gemm_stream(p, s));

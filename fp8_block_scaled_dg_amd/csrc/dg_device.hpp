@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dg_internal.hpp"
+
 namespace dg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -140,6 +142,59 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
   return v;
+}
+
+// ---- fused epilogue (bjdmk.com.cn DeepGEMM page, s3.2: activation and
+// residual applied while the product is in registers; pzsr.cn page, s2.3:
+// SwiGLU), in FP32 before the BF16 rounding ----
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
+
+__device__ __forceinline__ float act_f(float v, int act) {
+  switch (act) {
+    case EPI_RELU: return v > 0.0f ? v : 0.0f;
+    case EPI_SILU: return silu_f(v);
+    case EPI_GELU: return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    default: return v;
+  }
+}
+
+// Write the results t[0..3] of columns n .. n+3 (n % 4 == 0) of row m: the
+// activation, or SwiGLU over the column pairs (2j gate, 2j+1 up -> output
+// column j), then the residual, then BF16 round-to-nearest-even.
+__device__ __forceinline__ void store4(uint16_t* c, int64_t m, int64_t n, const float* t,
+                                       const Epilogue& e) {
+  if (e.act == EPI_SWIGLU) {
+    float o0 = silu_f(t[0]) * t[1];
+    float o1 = silu_f(t[2]) * t[3];
+    const int64_t idx = m * e.ldc + (n >> 1);
+    if (e.res) {
+      const uint32_t r = *reinterpret_cast<const uint32_t*>(e.res + idx);
+      o0 += bf16_bits_to_f32(r & 0xFFFFu);
+      o1 += bf16_bits_to_f32(r >> 16);
+    }
+    *reinterpret_cast<uint32_t*>(c + idx) = bf16_rne(o0) | (bf16_rne(o1) << 16);
+    return;
+  }
+  float o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = act_f(t[r], e.act);
+  const int64_t idx = m * e.ldc + n;
+  if (e.res) {
+    const uint2 r = *reinterpret_cast<const uint2*>(e.res + idx);
+    o[0] += bf16_bits_to_f32(r.x & 0xFFFFu);
+    o[1] += bf16_bits_to_f32(r.x >> 16);
+    o[2] += bf16_bits_to_f32(r.y & 0xFFFFu);
+    o[3] += bf16_bits_to_f32(r.y >> 16);
+  }
+  uint2 v;
+  v.x = bf16_rne(o[0]) | (bf16_rne(o[1]) << 16);
+  v.y = bf16_rne(o[2]) | (bf16_rne(o[3]) << 16);
+  *reinterpret_cast<uint2*>(c + idx) = v;
 }
 
 }  // namespace dg

@@ -15,6 +15,15 @@ hipError_t launch_quantize(uint8_t* q, float* scales, const float* x, int64_t ro
 hipError_t launch_quantize_ue8m0(uint8_t* q, uint32_t* sf, const float* x, int64_t rows,
                                  int64_t cols, int block_rows, hipStream_t stream);
 
+// Fused epilogue of the BF16 write-back (bjdmk.com.cn DeepGEMM page, s3.2;
+// SwiGLU per the pzsr.cn DeepGEMM page, s2.3).
+enum EpiAct { EPI_NONE = 0, EPI_RELU = 1, EPI_SILU = 2, EPI_GELU = 3, EPI_SWIGLU = 4 };
+struct Epilogue {
+  int act = EPI_NONE;
+  const uint16_t* res = nullptr;  // BF16 residual [M][ldc] (may be c itself), or null
+  int64_t ldc = 0;                // C row length: N, or N / 2 for SwiGLU (0: N)
+};
+
 struct GemmProblem {
   uint16_t* c;
   const uint8_t* a;
@@ -29,7 +38,15 @@ struct GemmProblem {
   // sa / sb (dense tiled kernel only), else nullptr
   const uint32_t* sfa = nullptr;
   const uint32_t* sfb = nullptr;
+  Epilogue epi;
 };
+
+// The epilogue with its row length filled in.
+inline Epilogue resolved_epilogue(const GemmProblem& q) {
+  Epilogue e = q.epi;
+  if (e.ldc == 0) e.ldc = e.act == EPI_SWIGLU ? q.N / 2 : q.N;
+  return e;
+}
 
 // Large-tile MFMA kernel (dense or grouped).
 hipError_t launch_gemm_tiled(const GemmProblem& p, bool grouped, hipStream_t stream);

@@ -47,6 +47,7 @@ __device__ int g_splitk_counters[kMaxCounters];
 
 struct SkinnyArgs {
   uint16_t* c;
+  Epilogue epi;
   const uint8_t* a;
   const float* af;  // FP32 A when the kernel quantises A itself, else null
   const uint8_t* b;
@@ -276,10 +277,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
       for (int f = 0; f < F; ++f) {
         const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
         if (n < p.N) {
-          uint2 v;
-          v.x = bf16_rne(acc[f][i][0]) | (bf16_rne(acc[f][i][1]) << 16);
-          v.y = bf16_rne(acc[f][i][2]) | (bf16_rne(acc[f][i][3]) << 16);
-          *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = v;
+          const float t[4] = {acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]};
+          store4(p.c, m, n, t, p.epi);
         }
       }
     }
@@ -329,6 +328,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   float4 sum[PJ];
   bool live[PJ];
   int64_t off[PJ];
+  int pm[PJ], pn[PJ];
 #pragma unroll
   for (int j = 0; j < PJ; ++j) {
     const int idx = threadIdx.x + 256 * j;
@@ -336,6 +336,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     const int cc = (idx - m * (BNT / 4)) * 4;
     live[j] = m < p.M && cc < ncols;
     off[j] = (int64_t)m * p.N + n0 + cc;
+    pm[j] = m;
+    pn[j] = n0 + cc;
     sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   for (int s0 = 0; s0 < p.S; s0 += G) {
@@ -372,10 +374,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
 #pragma unroll
   for (int j = 0; j < PJ; ++j) {
     if (!live[j]) continue;
-    uint2 v;
-    v.x = bf16_rne(sum[j].x) | (bf16_rne(sum[j].y) << 16);
-    v.y = bf16_rne(sum[j].z) | (bf16_rne(sum[j].w) << 16);
-    *reinterpret_cast<uint2*>(p.c + off[j]) = v;
+    const float t[4] = {sum[j].x, sum[j].y, sum[j].z, sum[j].w};
+    store4(p.c, pm[j], pn[j], t, p.epi);
   }
   if (threadIdx.x == 0)  // leave the counter zeroed for the next call
     __hip_atomic_store(&g_splitk_counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -444,6 +444,7 @@ hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, voi
                                       size_t workspace_bytes, hipStream_t stream) {
   SkinnyArgs p;
   p.c = q.c; p.a = nullptr; p.af = af; p.b = q.b; p.sa = nullptr; p.sb = q.sb;
+  p.epi = resolved_epilogue(q);
   p.a_block_rows = 1;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
   p.nkb = (int)(q.K / BK);
@@ -468,6 +469,7 @@ hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t work
                               hipStream_t stream) {
   SkinnyArgs p;
   p.c = q.c; p.a = q.a; p.af = nullptr; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.epi = resolved_epilogue(q);
   p.a_block_rows = q.a_block_rows;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
   p.nkb = (int)(q.K / BK);

@@ -33,6 +33,7 @@ constexpr int BK = 128;
 
 struct StreamArgs {
   uint16_t* c;
+  Epilogue epi;
   const uint8_t* a;
   const uint8_t* b;
   const float* sa;
@@ -153,12 +154,7 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(StreamArgs p) {
   auto store = [&](int f, int i, const float* t) {
     const int m = 16 * i + fr;
     const int n = n0 + 16 * f + 4 * g;
-    if (m < p.M && n < p.N) {
-      uint2 v;
-      v.x = bf16_rne(t[0]) | (bf16_rne(t[1]) << 16);
-      v.y = bf16_rne(t[2]) | (bf16_rne(t[3]) << 16);
-      *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = v;
-    }
+    if (m < p.M && n < p.N) store4(p.c, m, n, t, p.epi);
   };
   if (KS == 1) {
 #pragma unroll
@@ -245,6 +241,7 @@ bool stream_preferred(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_stream(const GemmProblem& q, hipStream_t stream) {
   StreamArgs p;
   p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.epi = resolved_epilogue(q);
   p.a_block_rows = q.a_block_rows;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
   p.nkb = (int)(q.K / BK);

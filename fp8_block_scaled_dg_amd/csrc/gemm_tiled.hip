@@ -57,6 +57,7 @@ struct TiledArgs {
   const uint32_t* sfb;
   const int32_t* m_indices;
   int num_groups;
+  Epilogue epi;  // dense only (grouped: none)
   int M, N, K;
   int nkb;        // K / 128
   int sa_stride;  // ceil(M / a_block_rows)
@@ -370,14 +371,12 @@ gemm_tiled_kernel(TiledArgs p) {
     for (int j = 0; j < 8; ++j) {
       const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
       if (n < p.N) {
-        uint2 v;
         if (zero_row) {
-          v = make_uint2(0, 0);
+          *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = make_uint2(0, 0);
         } else {
-          v.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-          v.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+          const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          store4(p.c, m, n, t, p.epi);
         }
-        *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = v;
       }
     }
   }
@@ -549,14 +548,12 @@ gemm_ring_kernel(TiledArgs p) {
     for (int j = 0; j < 8; ++j) {
       const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
       if (n < p.N) {
-        uint2 v;
         if (zero_row) {
-          v = make_uint2(0, 0);
+          *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = make_uint2(0, 0);
         } else {
-          v.x = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-          v.y = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+          const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          store4(p.c, m, n, t, p.epi);
         }
-        *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = v;
       }
     }
   }
@@ -568,6 +565,7 @@ hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   TiledArgs p;
   p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
   p.sfa = q.sfa; p.sfb = q.sfb;
+  p.epi = resolved_epilogue(q);
   p.m_indices = q.m_indices; p.num_groups = q.num_groups;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
   p.nkb = (int)(q.K / BK);

@@ -5,6 +5,7 @@
  * The operations follow two public pages:
  *   [Q] "DeepGEMM ... FP8 block-quantised GEMM" (lpnh.cn/news/2826317)
  *   [D] "DeepGEMM: GPU high-efficiency BLAS kernel library" (pzsr.cn/news/21800)
+ *   [M] "省算力新利器 DeepGEMM" (bjdmk.com.cn/news/5702840)
  *
  * Conventions for every entry point
  *   - All data pointers are DEVICE pointers owned by the caller; the library
@@ -40,7 +41,7 @@ enum {
     DG_OK = 0,
     DG_ERR_NULL = 1,        /* a required pointer is NULL                   */
     DG_ERR_SHAPE = 2,       /* a size is negative, zero or not a multiple   */
-    DG_ERR_UNSUPPORTED = 3, /* block_rows / group count not supported       */
+    DG_ERR_UNSUPPORTED = 3, /* block_rows / group count / epilogue unknown  */
     DG_ERR_ALIGN = 4,       /* a pointer is not suitably aligned            */
     DG_ERR_WORKSPACE = 5,   /* workspace given but smaller than required    */
     DG_ERR_HIP = 6          /* the HIP runtime reported an error            */
@@ -159,6 +160,38 @@ int dg_fp8_gemm_nt_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
 int dg_fp8_gemm_nt_fused_a(uint16_t *c, const float *a, const uint8_t *b, const float *sb,
                            int64_t M, int64_t N, int64_t K,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * NT GEMM with a fused epilogue [M s3.2: element-wise operators such as the
+ * activation and the residual connection applied to the product while it is
+ * still on chip, saving a write and a read of C; D s2.3: SwiGLU inside the
+ * MoE kernel].  The product is dg_fp8_gemm_nt's FP32 accumulator acc; then,
+ * in FP32, before the BF16 rounding:
+ *   act = DG_EPI_NONE   v = acc
+ *         DG_EPI_RELU   v = max(acc, 0)
+ *         DG_EPI_SILU   v = acc / (1 + exp(-acc))
+ *         DG_EPI_GELU   v = acc / 2 * (1 + erf(acc / sqrt(2)))
+ *         DG_EPI_SWIGLU B's rows interleave gate and up (row 2j gate, row
+ *                       2j+1 up): v[m][j] = silu(acc[m][2j]) * acc[m][2j+1],
+ *                       so C has N/2 columns
+ *   residual: optional BF16 [M][Nout] (Nout = N, or N/2 for SwiGLU),
+ *             16-byte aligned, added to v; it may be c itself (in place:
+ *             each element is read before it is written, by the same thread).
+ *   c : out, BF16 [M][Nout].  Everything else as dg_fp8_gemm_nt.
+ * An unknown act gives DG_ERR_UNSUPPORTED.  dg_fp8_gemm_nt is this call with
+ * DG_EPI_NONE and no residual.
+ */
+enum {
+    DG_EPI_NONE = 0,
+    DG_EPI_RELU = 1,
+    DG_EPI_SILU = 2,
+    DG_EPI_GELU = 3,
+    DG_EPI_SWIGLU = 4
+};
+int dg_fp8_gemm_nt_epilogue(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                            const float *sa, const float *sb, int a_block_rows,
+                            int64_t M, int64_t N, int64_t K, int act, const uint16_t *residual,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Grouped GEMM, experts contiguous along M [D s2.3, s3.2, s3.3]:

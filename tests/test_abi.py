@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     for need in ("dg_quantize_fp8_block", "dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contig",
                  "dg_abi_version", "dg_status_string", "dg_fp8_gemm_nt_workspace_bytes",
                  "dg_get_mk_alignment_for_contiguous_layout", "dg_fp8_gemm_nt_fused_a",
-                 "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0"):
+                 "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_fp8_gemm_nt_epilogue"):
         assert need in names
 
 
@@ -150,3 +150,18 @@ def test_ue8m0_validation(dg):
     assert ge(br=2) == 3
     assert ge(M=0) == 2 and ge(N=260) == 2 and ge(K=200) == 2
     assert ge(a=P1) == 4 and ge(sfb=ctypes.c_void_p(0x10002)) == 4
+
+
+def test_epilogue_validation(dg):
+    lib = dg.lib
+
+    def ge(act=0, res=None, **kw):
+        args = dict(c=P, a=P, b=P, sa=P, sb=P, br=128, M=256, N=256, K=256)
+        args.update(kw)
+        return lib.dg_fp8_gemm_nt_epilogue(args["c"], args["a"], args["b"], args["sa"], args["sb"],
+                                           args["br"], args["M"], args["N"], args["K"], act, res,
+                                           None, 0, None)
+    assert ge(act=5) == 3 and ge(act=-1) == 3
+    assert ge(res=P1) == 4
+    assert ge(c=None) == 1
+    assert ge(N=260) == 2
