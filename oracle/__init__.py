@@ -74,6 +74,9 @@ def _load():
     lib.orc_quantize_block_ue8m0.argtypes = [f32p, i64, i64, ctypes.c_int, u8p, u8p]
     lib.orc_ue8m0_pack.restype = None
     lib.orc_ue8m0_pack.argtypes = [u8p, i64, i64, ctypes.POINTER(ctypes.c_uint32)]
+    lib.orc_grouped_gemm_k.restype = ctypes.c_int
+    lib.orc_grouped_gemm_k.argtypes = [u8p, f32p, ctypes.c_int, u8p, f32p, i64p, ctypes.c_int,
+                                       i64, i64, i64, f64p]
     lib.orc_epilogue.restype = ctypes.c_int
     lib.orc_epilogue.argtypes = [f64p, i64, i64, ctypes.c_int, ctypes.POINTER(ctypes.c_uint16),
                                  f64p]
@@ -257,6 +260,26 @@ def grouped_gemm_contig(qa, sa, qb, sb, m_indices, a_block_rows: int = 128,
     if rc != 0:
         raise ValueError("oracle grouped_gemm_contig rejected its input")
     return ref
+
+
+def grouped_gemm_k(qa, sa, qb, sb, k_offsets, a_block_rows: int = 1) -> np.ndarray:
+    """K-grouped product (pzsr.cn DeepGEMM page s3.2, grouping along K for
+    MoE weight gradients): out[g] = A[:, k0:k1] . B[:, k0:k1]^T with
+    (k0, k1) = (k_offsets[g], k_offsets[g+1]), multiples of 128.
+    qa [M, K], qb [N, K]; sa [K/128, ceil(M/br)], sb [K/128, ceil(N/128)].
+    Returns float64 [G, M, N]."""
+    qa, sa, qb, sb, M, N, K = _check_gemm(qa, sa, a_block_rows, qb, sb)
+    assert sb.shape == (cdiv(K, 128), cdiv(N, 128))
+    ko = _c(k_offsets, np.int64)
+    G = ko.size - 1
+    out = np.empty((G, M, N), dtype=np.float64)
+    rc = _load().orc_grouped_gemm_k(_ptr(qa, ctypes.c_uint8), _ptr(sa, ctypes.c_float),
+                                    a_block_rows, _ptr(qb, ctypes.c_uint8),
+                                    _ptr(sb, ctypes.c_float), _ptr(ko, ctypes.c_int64), G, M, N, K,
+                                    _ptr(out, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle grouped_gemm_k rejected its input")
+    return out
 
 
 EPILOGUES = {"none": 0, "relu": 1, "silu": 2, "gelu": 3, "swiglu": 4}

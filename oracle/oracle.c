@@ -403,6 +403,42 @@ int orc_grouped_gemm_contig(const uint8_t *qa, const float *sa, int a_block_rows
     return 0;
 }
 
+/* K-grouped GEMM ("DeepGEMM: GPU high-efficiency BLAS kernel library",     */
+/* s3.2: grouped GEMM along the K axis, for MoE weight gradients): group g  */
+/* owns the K range [k_offsets[g], k_offsets[g+1]) (multiples of 128) and    */
+/* out[g] = A[:, range] . B[:, range]^T, with the scales of those K blocks.  */
+int orc_grouped_gemm_k(const uint8_t *qa, const float *sa, int a_block_rows,
+                       const uint8_t *qb, const float *sb, const int64_t *k_offsets,
+                       int num_groups, int64_t M, int64_t N, int64_t K, double *out)
+{
+    int64_t g, m, n, sa_stride, sb_stride;
+    if (check_gemm_args(qa, sa, a_block_rows, qb, sb, M, N, K) || !k_offsets || !out ||
+        num_groups < 1)
+        return -1;
+    sa_stride = ceil_div(M, a_block_rows);
+    sb_stride = ceil_div(N, 128);
+    for (g = 0; g < num_groups; ++g) {
+        int64_t k0 = k_offsets[g], k1 = k_offsets[g + 1];
+        if (k0 < 0 || k1 < k0 || k1 > K || k0 % 128 != 0 || k1 % 128 != 0)
+            return -1;
+        for (m = 0; m < M; ++m)
+            for (n = 0; n < N; ++n) {
+                double total = 0.0;
+                int64_t kb;
+                for (kb = k0 / 128; kb < k1 / 128; ++kb) {
+                    double part = 0.0;
+                    int64_t k;
+                    for (k = kb * 128; k < kb * 128 + 128; ++k)
+                        part += orc_e4m3_decode(qa[m * K + k]) * orc_e4m3_decode(qb[n * K + k]);
+                    total += (double)sa[kb * sa_stride + m / a_block_rows] *
+                             (double)sb[kb * sb_stride + n / 128] * part;
+                }
+                out[(g * M + m) * N + n] = total;
+            }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Epilogue fused into the GEMM's write-back ("省算力新利器 DeepGEMM",         */
 /* bjdmk.com.cn, s3.2: element-wise operators -- activations, residual add  */

@@ -97,6 +97,14 @@ int orc_grouped_gemm_contig(const uint8_t *qa, const float *sa, int a_block_rows
                             int64_t M, int64_t N, int64_t K,
                             int64_t rows_begin, int64_t rows_end, double *ref);
 
+/* K-grouped product (pzsr.cn page s3.2): group g covers K columns
+ * [k_offsets[g], k_offsets[g+1]) (multiples of 128, non-decreasing, within
+ * K); out [G][M][N] = per-group dequantised A . B^T over that range, FP64.
+ * A [M][K], B [N][K] K-major; scales as orc_gemm_nt over the whole K. */
+int orc_grouped_gemm_k(const uint8_t *qa, const float *sa, int a_block_rows,
+                       const uint8_t *qb, const float *sb, const int64_t *k_offsets,
+                       int num_groups, int64_t M, int64_t N, int64_t K, double *out);
+
 /* Epilogue on an FP64 product acc [M][N] (bjdmk.com.cn page s3.2; pzsr.cn
  * page s2.3 for SwiGLU): act 0 none, 1 relu, 2 silu, 3 gelu (erf form),
  * 4 swiglu (B rows interleaved gate/up: out[m][j] = silu(acc[m][2j]) *
