@@ -24,7 +24,8 @@ heavy-tailed, hot-channel activations and 1x128 activation scales),
 --config ue8m0 (the dense shapes with power-of-two block scales applied by the
 scaled matrix instruction), --config epilogue (SwiGLU and in-place residual
 fused into the write-back of MLP-shaped GEMMs, against the unfused pair),
---config copy (a plain device copy of known size, used to calibrate the
+--config wgrad (MoE weight gradient: token-major operands transposed, then
+the K-grouped GEMM), --config copy (a plain device copy of known size, used to calibrate the
 FETCH_SIZE/WRITE_SIZE counters), --config peak (the FP8 MFMA-loop probe: the
 matrix-core rate and shader clock this GPU sustains; the dense line also
 carries it as roofline.measured_peak).
@@ -524,6 +525,85 @@ class Epilogue:
         return None
 
 
+class WeightGrad:
+    """MoE weight gradient of the down projection (8 experts, 1024 tokens
+    top-2, hidden 4096, intermediate 11008): per expert g,
+    dW_g[4096][11008] = dY_g^T . H_g over that expert's tokens, i.e. a
+    K-grouped GEMM with K = the expert's token rows (padded to 128, the
+    routing of the MoE workload).  The operands arrive token-major (dY
+    [T][4096], H [T][11008], already quantised: 1x128 blocks along the token
+    axis for dY^T, 128x128 for H^T), so a step = transpose both code matrices
+    + the K-grouped GEMM."""
+    rot = 1
+
+    def __init__(self, dg, seed=0):
+        self.dg = dg
+        E, tokens, H, I = 8, 1024, 4096, 11008
+        r = datagen.moe_routing(tokens, E, 2, align=128, seed=seed)
+        padded = r["padded"]
+        ko = np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+        T = int(ko[-1])
+        self.M, self.N, self.K, self.G = H, I, T, E
+        a = datagen.normal((H, T), 1.0, seed=seed, stream=3)        # dY^T (logical [M][K])
+        b = datagen.normal((I, T), 1.0, seed=seed, stream=4)        # H^T  (logical [N][K])
+        qa, sa = dg.to_fp8(torch.from_numpy(a).cuda(), 1)
+        qb, sb = dg.to_fp8(torch.from_numpy(b).cuda(), 128)
+        # stored token-major, as a backward pass produces them
+        self.a_tok = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+        self.b_tok = torch.empty((T, I), dtype=torch.uint8, device="cuda")
+        dg.dg_transpose_fp8(self.a_tok, qa)
+        dg.dg_transpose_fp8(self.b_tok, qb)
+        self.sa, self.sb = sa, sb
+        self.qa = torch.empty((H, T), dtype=torch.uint8, device="cuda")
+        self.qb = torch.empty((I, T), dtype=torch.uint8, device="cuda")
+        self.ko = torch.from_numpy(ko).cuda()
+        self.c = torch.empty((E, H, I), dtype=torch.bfloat16, device="cuda")
+        self.flops = 2.0 * H * I * T
+        self.padded = [int(x) for x in padded]
+
+    def transposes(self):
+        self.dg.dg_transpose_fp8(self.qa, self.a_tok)
+        self.dg.dg_transpose_fp8(self.qb, self.b_tok)
+
+    def gemm(self):
+        self.dg.dg_fp8_grouped_gemm_k(self.c, self.qa, self.qb, self.sa, self.sb, 1, self.ko)
+
+    def step(self, i=0):
+        self.transposes()
+        self.gemm()
+
+    def outputs(self):
+        return [self.qa, self.qb, self.c]
+
+    def config(self):
+        return {"workload": "MoE weight gradient, K-grouped: 8 experts x dW[4096][11008] over each "
+                            "expert's token rows (1024 tokens top-2, padded to 128)",
+                "groups_k": self.padded, "mnk_total": [self.M, self.N, self.K],
+                "a_scales": "1x128 (along tokens)", "b_scales": "128x128",
+                "step": "transpose the token-major dY and H codes + K-grouped GEMM",
+                "inputs": "synthetic N(0,1) operands, uniform top-2 routing, seed 0"}
+
+    def breakdown(self, timer, reps):
+        tt = timer.time(self.transposes, reps, key=("wt",), calls=4)
+        tg = timer.time(self.gemm, reps, key=("wg",), calls=2)
+        tbytes = 2 * (self.M + self.N) * self.K
+        return [{"transposes_us": tt * 1e3, "transpose_gbs": tbytes / (tt * 1e-3) / 1e9,
+                 "gemm_us": tg * 1e3, "gemm_tflops": self.flops / (tg * 1e-3) / 1e12}]
+
+    def roofline(self, timer, reps):
+        st = timer.stats(self.gemm, max(reps, 25), ("wg",), calls=2)
+        t = st["mean"] * 1e-3
+        ach = self.flops / (t * 1e-3) / 1e12
+        return {"kernel": "gemm_tiled_kernel<256,1,false,false,true> K-grouped %dx%dx%d, 8 groups"
+                          % (self.M, self.N, self.K),
+                "bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_FP8_TFLOPS, "traffic": None, "avg_launch_us": t * 1e3,
+                "launch_us_stats": st}
+
+    def cpu_baseline(self):
+        return None
+
+
 class Moe:
     rot = 1
 
@@ -689,7 +769,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="dense",
                     choices=["dense", "decode", "moe", "small", "outlier", "ue8m0", "epilogue",
-                             "copy", "peak"])
+                             "wgrad", "copy", "peak"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -725,6 +805,8 @@ def main():
         w = Dense(dg, DENSE, ue8m0=True)
     elif args.config == "epilogue":
         w = Epilogue(dg)
+    elif args.config == "wgrad":
+        w = WeightGrad(dg)
     elif args.config == "decode":
         w = Decode(dg)
     else:

@@ -58,6 +58,15 @@ def _load():
     lib.dg_fp8_gemm_nt_epilogue.restype = i32
     lib.dg_fp8_gemm_nt_epilogue.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp, vp,
                                             ctypes.c_size_t, vp]
+    lib.dg_transpose_fp8.restype = i32
+    lib.dg_transpose_fp8.argtypes = [vp, vp, i64, i64, vp]
+    lib.dg_fp8_gemm_workspace_bytes.restype = ctypes.c_size_t
+    lib.dg_fp8_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    lib.dg_fp8_gemm.restype = i32
+    lib.dg_fp8_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp, ctypes.c_size_t,
+                                vp]
+    lib.dg_fp8_grouped_gemm_k.restype = i32
+    lib.dg_fp8_grouped_gemm_k.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
     lib.dg_fp8_gemm_nt_fused_a.restype = i32
     lib.dg_fp8_gemm_nt_fused_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t,
                                            vp]
@@ -270,6 +279,72 @@ def dg_fp8_gemm_nt_epilogue(c, a, b, sa, sb, a_block_rows: int = 128, act: str =
            "dg_fp8_gemm_nt_epilogue")
 
 
+LAYOUTS = {"nt": 0, "tn": 1, "nn": 2, "tt": 3}
+
+
+def dg_transpose_fp8(out, inp, stream=None) -> None:
+    """out [cols, rows] = inp [rows, cols]^T (bytes; rows, cols multiples of 16)."""
+    out = _codes(out, "out")
+    inp = _codes(inp, "inp")
+    rows, cols = inp.shape
+    if out.shape != (cols, rows):
+        raise ValueError("out must be [cols, rows]")
+    _check(lib.dg_transpose_fp8(_ptr(out), _ptr(inp), rows, cols, _stream(stream)),
+           "dg_transpose_fp8")
+
+
+def dg_fp8_gemm_workspace_bytes(M: int, N: int, K: int, layout: str = "nt") -> int:
+    return lib.dg_fp8_gemm_workspace_bytes(M, N, K, LAYOUTS[layout])
+
+
+def dg_fp8_gemm(c, a, b, sa, sb, a_block_rows: int = 128, layout: str = "nt", workspace=None,
+                stream=None) -> None:
+    """C[M,N] = A . B^T with operands stored per ``layout`` (first letter A:
+    n = [M,K], t = [K,M]; second letter B: t = [N,K], n = [K,N])."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sa, torch.float32, "sa")
+    _require(sb, torch.float32, "sb")
+    M, N = c.shape
+    a_t = layout in ("tn", "tt")
+    b_n = layout in ("tn", "nn")
+    K = a.shape[0] if a_t else a.shape[1]
+    if a.shape != ((K, M) if a_t else (M, K)) or b.shape != ((K, N) if b_n else (N, K)):
+        raise ValueError("shape mismatch for layout %s: a %s, b %s, c %s"
+                         % (layout, tuple(a.shape), tuple(b.shape), tuple(c.shape)))
+    if sa.numel() != cdiv(K, 128) * cdiv(M, a_block_rows):
+        raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
+    if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
+    _check(lib.dg_fp8_gemm(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), a_block_rows, M, N, K,
+                           LAYOUTS[layout], _ptr(workspace), _workspace_bytes(workspace),
+                           _stream(stream)), "dg_fp8_gemm")
+
+
+def dg_fp8_grouped_gemm_k(c, a, b, sa, sb, a_block_rows: int, k_offsets, stream=None) -> None:
+    """K-grouped: c [G, M, N] (bf16), a [M, K], b [N, K], k_offsets int64
+    device [G + 1] (multiples of 128): c[g] = A[:, k0:k1] . B[:, k0:k1]^T."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sa, torch.float32, "sa")
+    _require(sb, torch.float32, "sb")
+    _require(k_offsets, torch.int64, "k_offsets")
+    M, K = a.shape
+    N = b.shape[0]
+    G = k_offsets.numel() - 1
+    if b.shape[1] != K or c.shape != (G, M, N):
+        raise ValueError("shape mismatch")
+    if sa.numel() != cdiv(K, 128) * cdiv(M, a_block_rows):
+        raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
+    if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
+    _check(lib.dg_fp8_grouped_gemm_k(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), a_block_rows,
+                                     _ptr(k_offsets), G, M, N, K, _stream(stream)),
+           "dg_fp8_grouped_gemm_k")
+
+
 def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices,
                                stream=None) -> None:
     """Grouped M-contiguous: a [M,K], b [G,N,K], sb [G,K/128,ceil(N/128)],
@@ -334,5 +409,6 @@ __all__ = [
     "dg_quantize_fp8_block", "dg_fp8_gemm_nt_workspace_bytes", "dg_fp8_gemm_nt",
     "dg_fp8_gemm_nt_fused_a", "FUSED_A_MAX_M", "dg_fp8_grouped_gemm_contig", "to_fp8",
     "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "to_fp8_ue8m0",
-    "dg_fp8_gemm_nt_epilogue", "EPILOGUES", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
+    "dg_fp8_gemm_nt_epilogue", "EPILOGUES", "dg_transpose_fp8", "dg_fp8_gemm_workspace_bytes",
+    "dg_fp8_gemm", "LAYOUTS", "dg_fp8_grouped_gemm_k", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
 ]

@@ -46,6 +46,15 @@ int check_workspace(int64_t M, int64_t N, int64_t K, void** workspace, size_t* w
   return DG_OK;
 }
 
+size_t align16(int64_t n) { return (size_t)((n + 15) / 16 * 16); }
+
+// Workspace bytes for the operands a layout has to transpose.
+size_t transpose_bytes(int64_t M, int64_t N, int64_t K, int layout) {
+  const bool a_t = layout == DG_LAYOUT_TN || layout == DG_LAYOUT_TT;
+  const bool b_n = layout == DG_LAYOUT_TN || layout == DG_LAYOUT_NN;
+  return (a_t ? align16(M * K) : 0) + (b_n ? align16(N * K) : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +171,78 @@ int dg_fp8_gemm_nt_fused_a(uint16_t* c, const float* a, const uint8_t* b, const 
   dg::GemmProblem p{c, nullptr, b, nullptr, sb, nullptr, 1, 1, M, N, K};
   return from_hip(dg::launch_gemm_skinny_fused_a(p, a, workspace, workspace_bytes,
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int dg_transpose_fp8(uint8_t* out, const uint8_t* in, int64_t rows, int64_t cols, void* stream) {
+  if (!out || !in) return DG_ERR_NULL;
+  if (rows < 16 || cols < 16 || rows % 16 != 0 || cols % 16 != 0) return DG_ERR_SHAPE;
+  if ((rows + 127) / 128 > kMaxGridY || (cols + 127) / 128 > INT32_MAX) return DG_ERR_SHAPE;
+  if (rows > INT64_MAX / cols) return DG_ERR_SHAPE;
+  if (!aligned(out, 16) || !aligned(in, 16)) return DG_ERR_ALIGN;
+  const uint8_t* o = out;
+  if (o < in + rows * cols && in < o + rows * cols) return DG_ERR_UNSUPPORTED;  // overlap
+  return from_hip(dg::launch_transpose_u8(out, in, rows, cols, static_cast<hipStream_t>(stream)));
+}
+
+size_t dg_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout) {
+  if (M < 1 || N < 1 || K < 1 || layout < DG_LAYOUT_NT || layout > DG_LAYOUT_TT) return 0;
+  return transpose_bytes(M, N, K, layout) + dg_fp8_gemm_nt_workspace_bytes(M, N, K);
+}
+
+int dg_fp8_gemm(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa, const float* sb,
+                int a_block_rows, int64_t M, int64_t N, int64_t K, int layout, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (layout < DG_LAYOUT_NT || layout > DG_LAYOUT_TT) return DG_ERR_UNSUPPORTED;
+  if (layout == DG_LAYOUT_NT)
+    return dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, M, N, K, workspace, workspace_bytes,
+                          stream);
+  int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
+  if (st != DG_OK) return st;
+  const bool a_t = layout == DG_LAYOUT_TN || layout == DG_LAYOUT_TT;  // A given [K][M]
+  const bool b_n = layout == DG_LAYOUT_TN || layout == DG_LAYOUT_NN;  // B given [K][N]
+  if ((a_t && M % 16 != 0) || (b_n && N % 16 != 0)) return DG_ERR_SHAPE;
+  if ((a_t && (K + 127) / 128 > kMaxGridY) || (b_n && (K + 127) / 128 > kMaxGridY))
+    return DG_ERR_SHAPE;
+  const size_t tb = transpose_bytes(M, N, K, layout);
+  if (!workspace || workspace_bytes < tb) return DG_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return DG_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* ak = a;
+  const uint8_t* bk = b;
+  size_t used = 0;
+  if (a_t) {
+    st = from_hip(dg::launch_transpose_u8(ws, a, K, M, s));  // [K][M] -> [M][K]
+    if (st != DG_OK) return st;
+    ak = ws;
+    used += align16(M * K);
+  }
+  if (b_n) {
+    st = from_hip(dg::launch_transpose_u8(ws + used, b, K, N, s));  // [K][N] -> [N][K]
+    if (st != DG_OK) return st;
+    bk = ws + used;
+    used += align16(N * K);
+  }
+  // the rest of the workspace, if large enough, serves the small-M split-K plan
+  void* rest = workspace_bytes > used ? ws + used : nullptr;
+  return dg_fp8_gemm_nt(c, ak, bk, sa, sb, a_block_rows, M, N, K, rest,
+                        rest ? workspace_bytes - used : 0, stream);
+}
+
+int dg_fp8_grouped_gemm_k(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
+                          const float* sb, int a_block_rows, const int64_t* k_offsets,
+                          int num_groups, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
+  if (st != DG_OK) return st;
+  if (!k_offsets) return DG_ERR_NULL;
+  if (!aligned(k_offsets, 8)) return DG_ERR_ALIGN;
+  if (num_groups < 1) return DG_ERR_UNSUPPORTED;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles * num_groups > INT32_MAX) return DG_ERR_SHAPE;
+  if (M * N > INT64_MAX / num_groups) return DG_ERR_SHAPE;
+  dg::GemmProblem p{c, a, b, sa, sb, nullptr, num_groups, a_block_rows, M, N, K};
+  p.k_offsets = k_offsets;
+  return from_hip(dg::launch_gemm_tiled_kgrouped(p, static_cast<hipStream_t>(stream)));
 }
 
 int dg_fp8_grouped_gemm_contig(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,

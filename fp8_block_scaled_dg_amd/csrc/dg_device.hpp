@@ -163,38 +163,82 @@ __device__ __forceinline__ float act_f(float v, int act) {
   }
 }
 
-// Write the results t[0..3] of columns n .. n+3 (n % 4 == 0) of row m: the
-// activation, or SwiGLU over the column pairs (2j gate, 2j+1 up -> output
-// column j), then the residual, then BF16 round-to-nearest-even.
-__device__ __forceinline__ void store4(uint16_t* c, int64_t m, int64_t n, const float* t,
-                                       const Epilogue& e) {
-  if (e.act == EPI_SWIGLU) {
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
+
+// The results t[0..3] of columns n .. n+3 (n % 4 == 0) of row m after the
+// epilogue ACT (an EpiAct; SwiGLU pairs the columns: 2j gate, 2j+1 up ->
+// output column j), then the residual if RES, then BF16 round-to-nearest-
+// even.  Returns the number of output columns (4, or 2 for SwiGLU, packed in
+// v.x); the first one is column n, or n / 2 for SwiGLU.
+template <int ACT, bool RES>
+__device__ __forceinline__ int epilogue4(int64_t m, int64_t n, const float* t, const Epilogue& e,
+                                         uint2& v) {
+  if constexpr (ACT == EPI_SWIGLU) {
     float o0 = silu_f(t[0]) * t[1];
     float o1 = silu_f(t[2]) * t[3];
-    const int64_t idx = m * e.ldc + (n >> 1);
-    if (e.res) {
-      const uint32_t r = *reinterpret_cast<const uint32_t*>(e.res + idx);
+    if constexpr (RES) {
+      const uint32_t r = *reinterpret_cast<const uint32_t*>(e.res + m * e.ldc + (n >> 1));
       o0 += bf16_bits_to_f32(r & 0xFFFFu);
       o1 += bf16_bits_to_f32(r >> 16);
     }
-    *reinterpret_cast<uint32_t*>(c + idx) = bf16_rne(o0) | (bf16_rne(o1) << 16);
-    return;
-  }
-  float o[4];
+    v.x = bf16_rne(o0) | (bf16_rne(o1) << 16);
+    v.y = 0;
+    return 2;
+  } else {
+    float o[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) o[r] = act_f(t[r], e.act);
-  const int64_t idx = m * e.ldc + n;
-  if (e.res) {
-    const uint2 r = *reinterpret_cast<const uint2*>(e.res + idx);
-    o[0] += bf16_bits_to_f32(r.x & 0xFFFFu);
-    o[1] += bf16_bits_to_f32(r.x >> 16);
-    o[2] += bf16_bits_to_f32(r.y & 0xFFFFu);
-    o[3] += bf16_bits_to_f32(r.y >> 16);
+    for (int r = 0; r < 4; ++r) o[r] = act_f(t[r], ACT);
+    if constexpr (RES) {
+      const uint2 r = *reinterpret_cast<const uint2*>(e.res + m * e.ldc + n);
+      o[0] += bf16_bits_to_f32(r.x & 0xFFFFu);
+      o[1] += bf16_bits_to_f32(r.x >> 16);
+      o[2] += bf16_bits_to_f32(r.y & 0xFFFFu);
+      o[3] += bf16_bits_to_f32(r.y >> 16);
+    }
+    v.x = bf16_rne(o[0]) | (bf16_rne(o[1]) << 16);
+    v.y = bf16_rne(o[2]) | (bf16_rne(o[3]) << 16);
+    return 4;
   }
+}
+
+// epilogue4, written straight to C [.][ldc].
+template <int ACT, bool RES>
+__device__ __forceinline__ void store4(uint16_t* c, int64_t m, int64_t n, const float* t,
+                                       const Epilogue& e) {
   uint2 v;
-  v.x = bf16_rne(o[0]) | (bf16_rne(o[1]) << 16);
-  v.y = bf16_rne(o[2]) | (bf16_rne(o[3]) << 16);
-  *reinterpret_cast<uint2*>(c + idx) = v;
+  if (epilogue4<ACT, RES>(m, n, t, e, v) == 2)
+    *reinterpret_cast<uint32_t*>(c + m * e.ldc + (n >> 1)) = v.x;
+  else
+    *reinterpret_cast<uint2*>(c + m * e.ldc + n) = v;
+}
+
+// Runs f(IntTag<ACT>, IntTag<RES>) for the epilogue e, choosing the variant
+// once per store loop: with the choice made per element, every store site
+// carries every variant inline and the epilogue path sprawls over the
+// instruction cache (measured: ~16 us more per 256 x 256 tile).
+template <class F>
+__device__ __forceinline__ void with_epilogue(const Epilogue& e, F&& f) {
+  const bool r = e.res != nullptr;
+  switch (e.act) {
+    case EPI_RELU:
+      if (r) f(IntTag<EPI_RELU>{}, IntTag<1>{}); else f(IntTag<EPI_RELU>{}, IntTag<0>{});
+      break;
+    case EPI_SILU:
+      if (r) f(IntTag<EPI_SILU>{}, IntTag<1>{}); else f(IntTag<EPI_SILU>{}, IntTag<0>{});
+      break;
+    case EPI_GELU:
+      if (r) f(IntTag<EPI_GELU>{}, IntTag<1>{}); else f(IntTag<EPI_GELU>{}, IntTag<0>{});
+      break;
+    case EPI_SWIGLU:
+      if (r) f(IntTag<EPI_SWIGLU>{}, IntTag<1>{}); else f(IntTag<EPI_SWIGLU>{}, IntTag<0>{});
+      break;
+    default:
+      if (r) f(IntTag<EPI_NONE>{}, IntTag<1>{}); else f(IntTag<EPI_NONE>{}, IntTag<0>{});
+      break;
+  }
 }
 
 }  // namespace dg

@@ -24,6 +24,10 @@ struct Epilogue {
   int64_t ldc = 0;                // C row length: N, or N / 2 for SwiGLU (0: N)
 };
 
+// out [cols][rows] = transpose of in [rows][cols] (bytes); rows, cols % 16 == 0.
+hipError_t launch_transpose_u8(uint8_t* out, const uint8_t* in, int64_t rows, int64_t cols,
+                               hipStream_t stream);
+
 struct GemmProblem {
   uint16_t* c;
   const uint8_t* a;
@@ -39,6 +43,8 @@ struct GemmProblem {
   const uint32_t* sfa = nullptr;
   const uint32_t* sfb = nullptr;
   Epilogue epi;
+  // K-grouped (num_groups outputs, group g over K [k_offsets[g], k_offsets[g+1]))
+  const int64_t* k_offsets = nullptr;
 };
 
 // The epilogue with its row length filled in.
@@ -50,6 +56,8 @@ inline Epilogue resolved_epilogue(const GemmProblem& q) {
 
 // Large-tile MFMA kernel (dense or grouped).
 hipError_t launch_gemm_tiled(const GemmProblem& p, bool grouped, hipStream_t stream);
+// Dense 256 x 256 tile kernel over K groups: C[g] = A[:, Kg] . B[:, Kg]^T.
+hipError_t launch_gemm_tiled_kgrouped(const GemmProblem& p, hipStream_t stream);
 // Dense 256 x 256 tile kernel with UE8M0 scales applied by the scaled MFMA.
 hipError_t launch_gemm_tiled_ue8m0(const GemmProblem& p, hipStream_t stream);
 

@@ -269,19 +269,21 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
 
   // lane owns C[m = 16i + l%16][n = n0 + 16*F*wave + 16f + 4*(l/16) + r]
   if (p.S == 1) {
+    with_epilogue(p.epi, [&](auto act, auto res) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int m = 16 * i + fr;
-      if (m >= p.M) continue;
+      for (int i = 0; i < NI; ++i) {
+        const int m = 16 * i + fr;
+        if (m >= p.M) continue;
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
-        if (n < p.N) {
-          const float t[4] = {acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]};
-          store4(p.c, m, n, t, p.epi);
+        for (int f = 0; f < F; ++f) {
+          const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
+          if (n < p.N) {
+            const float t[4] = {acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]};
+            store4<decltype(act)::value, decltype(res)::value != 0>(p.c, m, n, t, p.epi);
+          }
         }
       }
-    }
+    });
     return;
   }
 
@@ -371,12 +373,14 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
         }
       }
   }
+  with_epilogue(p.epi, [&](auto act, auto res) {
 #pragma unroll
-  for (int j = 0; j < PJ; ++j) {
-    if (!live[j]) continue;
-    const float t[4] = {sum[j].x, sum[j].y, sum[j].z, sum[j].w};
-    store4(p.c, pm[j], pn[j], t, p.epi);
-  }
+    for (int j = 0; j < PJ; ++j) {
+      if (!live[j]) continue;
+      const float t[4] = {sum[j].x, sum[j].y, sum[j].z, sum[j].w};
+      store4<decltype(act)::value, decltype(res)::value != 0>(p.c, pm[j], pn[j], t, p.epi);
+    }
+  });
   if (threadIdx.x == 0)  // leave the counter zeroed for the next call
     __hip_atomic_store(&g_splitk_counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -151,19 +151,21 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(StreamArgs p) {
   }
 
   // lane owns C[m = 16i + l%16][n = n0 + 16f + 4*(l/16) + r]
-  auto store = [&](int f, int i, const float* t) {
+  auto store = [&](auto act, auto res, int f, int i, const float* t) {
     const int m = 16 * i + fr;
     const int n = n0 + 16 * f + 4 * g;
-    if (m < p.M && n < p.N) store4(p.c, m, n, t, p.epi);
+    if (m < p.M && n < p.N) store4<decltype(act)::value, decltype(res)::value != 0>(p.c, m, n, t, p.epi);
   };
   if (KS == 1) {
+    with_epilogue(p.epi, [&](auto act, auto res) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float t[4] = {acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]};
-        store(f, i, t);
-      }
+        for (int i = 0; i < NI; ++i) {
+          const float t[4] = {acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]};
+          store(act, res, f, i, t);
+        }
+    });
     return;
   }
   // KS > 1: the workgroup is one strip (SPW == 1 needs KS == 4; KS == 2 gives
@@ -176,19 +178,21 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(StreamArgs p) {
       for (int r = 0; r < 4; ++r) red[wave][f][i][r][lane] = acc[f][i][r];
   __syncthreads();
   if (kpart != 0) return;
+  with_epilogue(p.epi, [&](auto act, auto res) {
 #pragma unroll
-  for (int f = 0; f < NF; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float t[4];
+      for (int i = 0; i < NI; ++i) {
+        float t[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        t[r] = red[wave][f][i][r][lane];
+        for (int r = 0; r < 4; ++r) {
+          t[r] = red[wave][f][i][r][lane];
 #pragma unroll
-        for (int w = 1; w < KS; ++w) t[r] += red[wave + w][f][i][r][lane];
+          for (int w = 1; w < KS; ++w) t[r] += red[wave + w][f][i][r][lane];
+        }
+        store(act, res, f, i, t);
       }
-      store(f, i, t);
-    }
+  });
 }
 
 template <int RW, int MP, int KS, int U>

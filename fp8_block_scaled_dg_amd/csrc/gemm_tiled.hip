@@ -56,6 +56,7 @@ struct TiledArgs {
   const uint32_t* sfa;  // UE8M0 variant: packed exponent words instead of sa / sb
   const uint32_t* sfb;
   const int32_t* m_indices;
+  const int64_t* k_offsets;  // K-grouped: group g covers K [k_offsets[g], k_offsets[g+1])
   int num_groups;
   Epilogue epi;  // dense only (grouped: none)
   int M, N, K;
@@ -132,11 +133,17 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
 // so concurrently running tiles share A and B panels.  Grouped: N-tile-major,
 // so the tiles that read one expert's B tile (all its row blocks) run back to
 // back on the same XCD and the B tile comes from HBM once.
-__device__ __forceinline__ void map_tile(const TiledArgs& p, bool grouped, int& tm, int& tn) {
+__device__ __forceinline__ void map_tile(const TiledArgs& p, bool grouped, int& tm, int& tn,
+                                         int groups = 1, int* kgroup = nullptr) {
   const int bid = blockIdx.x;
-  const int total = p.tiles_m * p.tiles_n;
+  const int per_g = p.tiles_m * p.tiles_n;
+  const int total = per_g * groups;
   const int x = bid & 7, per = total >> 3, extra = total & 7;
-  const int L = x * per + min(x, extra) + (bid >> 3);
+  int L = x * per + min(x, extra) + (bid >> 3);
+  if (kgroup) {  // K-grouped: consecutive positions stay within one group's tiles
+    *kgroup = L / per_g;
+    L -= *kgroup * per_g;
+  }
   if (grouped) {
     tn = L / p.tiles_m;
     tm = L - tn * p.tiles_m;
@@ -199,7 +206,11 @@ __device__ __forceinline__ bool grouped_tile(const TiledArgs& p, int blk, int n0
 // passes the exponent byte of the row it feeds (one byte per 32 products of
 // that row; a 128-K block uses the same byte for all four) -- so the
 // accumulators chain through K with no partials and no promotion FMAs.
-template <int BM, int A_BLK, bool GROUPED, bool E8 = false>
+// KG: K-grouped (DeepGEMM page on pzsr.cn, s3.2: grouping along K, the MoE
+// weight-gradient layout): the grid covers num_groups x the output tiles;
+// group g runs the K blocks [k_offsets[g] / 128, k_offsets[g+1] / 128) and
+// writes C + g * M * N (an empty range writes zeros).
+template <int BM, int A_BLK, bool GROUPED, bool E8 = false, bool KG = false>
 __global__ void __launch_bounds__(BM * BN / 128)
 gemm_tiled_kernel(TiledArgs p) {
   constexpr int WM = BM / 64;
@@ -214,11 +225,23 @@ gemm_tiled_kernel(TiledArgs p) {
   const int wm = wave % WM;
   const int wn = wave / WM;
 
-  int tm, tn;
-  map_tile(p, GROUPED, tm, tn);
+  int tm, tn, kgroup = 0;
+  map_tile(p, GROUPED, tm, tn, KG ? p.num_groups : 1, KG ? &kgroup : nullptr);
   const int n0 = tn * BN;
   int m0 = tm * BM;
   int rows_end = p.M;  // rows [m0, rows_end) are stored
+  int kb_begin = 0, kb_end = p.nkb;
+  uint16_t* cbase = p.c;
+  if (KG) {
+    // clamped into [0, nkb]: offsets that break the contract give wrong sums,
+    // never reads outside A, B or the scales
+    int64_t k0 = p.k_offsets[kgroup] / BK, k1 = p.k_offsets[kgroup + 1] / BK;
+    k0 = k0 < 0 ? 0 : (k0 > p.nkb ? p.nkb : k0);
+    k1 = k1 < k0 ? k0 : (k1 > p.nkb ? p.nkb : k1);
+    kb_begin = (int)k0;
+    kb_end = (int)k1;
+    cbase += (int64_t)kgroup * p.M * p.N;
+  }
 
   const uint8_t* bbase = p.b;
   const float* sbbase = p.sb;
@@ -266,21 +289,23 @@ gemm_tiled_kernel(TiledArgs p) {
     eb_cur = (int)(p.sfb[nb] & 0xFFu);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa_cur[i] = p.sa[sa_idx[i]];
-    sb_cur = sbbase[nb];
+    for (int i = 0; i < 4; ++i) sa_cur[i] = p.sa[(int64_t)kb_begin * p.sa_stride + sa_idx[i]];
+    sb_cur = sbbase[(int64_t)kb_begin * p.sb_stride + nb];
   }
 
-  lda.issue(p.a, lds0, wave, 0);
-  ldb.issue(bbase, lds0 + A_BYTES, wave, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  if (kb_end > kb_begin) {  // uniform per workgroup (false only for an empty K group)
+    lda.issue(p.a, lds0, wave, kb_begin);
+    ldb.issue(bbase, lds0 + A_BYTES, wave, kb_begin);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
 
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
   auto step = [&](const uint8_t* cur, uint8_t* nxt, int kb) {
     // The last step re-stages the final K slice into the idle buffer so the
     // body stays one basic block (the scheduling hints below need that).
-    const int kn = kb + 1 < p.nkb ? kb + 1 : kb;
+    const int kn = kb + 1 < kb_end ? kb + 1 : kb;
     float s[4];
     if constexpr (E8) {
       const int w = kn >> 2, sh = 8 * (kn & 3);
@@ -355,28 +380,84 @@ gemm_tiled_kernel(TiledArgs p) {
     __syncthreads();
   };
 
-  for (int kb = 0; kb < p.nkb; kb += 2) {
+  for (int kb = kb_begin; kb < kb_end; kb += 2) {
     step(lds0, lds1, kb);
-    if (kb + 1 < p.nkb) step(lds1, lds0, kb + 1);
+    if (kb + 1 < kb_end) step(lds1, lds0, kb + 1);
   }
 
-  // epilogue: BF16 round-to-nearest-even, 4 consecutive columns per lane
+  if constexpr (GROUPED) {
+    // epilogue: BF16 round-to-nearest-even, 4 consecutive columns per lane
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 64 + 16 * i + fr;
-    if (m >= rows_end) continue;
-    bool zero_row = false;
-    if (GROUPED) zero_row = p.m_indices[m] < 0;
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 64 + 16 * i + fr;
+      if (m >= rows_end) continue;
+      const bool zero_row = p.m_indices[m] < 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
-      if (n < p.N) {
-        if (zero_row) {
-          *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = make_uint2(0, 0);
-        } else {
-          const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-          store4(p.c, m, n, t, p.epi);
+      for (int j = 0; j < 8; ++j) {
+        const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
+        if (n < p.N) {
+          if (zero_row) {
+            *reinterpret_cast<uint2*>(cbase + (int64_t)m * p.N + n) = make_uint2(0, 0);
+          } else {
+            const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            store4<EPI_NONE, false>(cbase, m, n, t, p.epi);  // grouped: no epilogue
+          }
         }
+      }
+    }
+  } else {
+    // The finished tile leaves through LDS.  Stored straight from the MFMA
+    // layout, each store instruction writes 32 bytes into each of 16 rows;
+    // when C does not fit in the Infinity Cache those scattered pieces cap
+    // the write rate far below HBM's.  Staged, every instruction writes whole
+    // 512-byte row segments.  Staged row r (BF16, ocols per row) sits in lds0
+    // (r < 128) or lds1 at (r % 128) * rowb, its 16-byte chunk c at chunk
+    // c ^ (r % chunks) (the 16 rows of one MFMA-layout write hit distinct
+    // banks; the row-wise reads are conflict-free either way).  The K loop
+    // ended with a barrier after its last LDS read and DMA.
+    const bool glu = p.epi.act == EPI_SWIGLU;
+    const int rowb = glu ? BN : 2 * BN;  // bytes per staged row
+    const int chunks = rowb / 16;
+    with_epilogue(p.epi, [&](auto act, auto res) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 64 + 16 * i + fr;
+        const int m = m0 + r < rows_end ? m0 + r : rows_end - 1;  // (row not stored)
+        uint8_t* row = (r < 128 ? lds0 : lds1) + (r & 127) * rowb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int nl = wn * 128 + 16 * j + 4 * (lane >> 4);
+          const int n = n0 + nl < p.N ? n0 + nl : p.N - 4;  // (column not stored)
+          const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          uint2 v;
+          const int cnt =
+              epilogue4<decltype(act)::value, decltype(res)::value != 0>(m, n, t, p.epi, v);
+          const int ob = (cnt == 2 ? nl : 2 * nl);  // byte offset of the first output column
+          uint8_t* dst = row + ((((ob >> 4) ^ (r % chunks)) << 4) | (ob & 15));
+          if (cnt == 2)
+            *reinterpret_cast<uint32_t*>(dst) = v.x;
+          else
+            *reinterpret_cast<uint2*>(dst) = v;
+        }
+      }
+    });
+    __syncthreads();
+    const int64_t ldc = p.epi.ldc;
+    const int64_t oc0 = glu ? n0 / 2 : n0;  // first output column of the tile
+    const bool wide = (ldc & 7) == 0;       // 16-byte stores stay aligned
+    for (int q = threadIdx.x; q < BM * chunks; q += BM * BN / 128) {
+      const int r = q / chunks, cc = q - r * chunks;
+      const int64_t m = m0 + r;
+      const int64_t col = oc0 + 8 * cc;
+      if (m >= rows_end || col >= ldc) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>((r < 128 ? lds0 : lds1) + (r & 127) * rowb +
+                                                       ((cc ^ (r % chunks)) << 4));
+      uint16_t* g = cbase + m * ldc + col;
+      if (wide && col + 8 <= ldc) {
+        *reinterpret_cast<uint4*>(g) = v;
+      } else {
+        *reinterpret_cast<uint2*>(g) = make_uint2(v.x, v.y);
+        if (col + 8 <= ldc) *reinterpret_cast<uint2*>(g + 4) = make_uint2(v.z, v.w);
       }
     }
   }
@@ -552,21 +633,23 @@ gemm_ring_kernel(TiledArgs p) {
           *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = make_uint2(0, 0);
         } else {
           const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-          store4(p.c, m, n, t, p.epi);
+          store4<EPI_NONE, false>(p.c, m, n, t, p.epi);
         }
       }
     }
   }
 }
 
-template <bool RING, int A_BLK, bool GROUPED, bool E8 = false>
+template <bool RING, int A_BLK, bool GROUPED, bool E8 = false, bool KG = false>
 hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   static_assert(!(E8 && (RING || GROUPED)), "UE8M0 scales: dense two-stage kernel only");
+  static_assert(!(KG && (RING || GROUPED || E8)), "K-grouped: dense two-stage kernel only");
   TiledArgs p;
   p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
   p.sfa = q.sfa; p.sfb = q.sfb;
   p.epi = resolved_epilogue(q);
   p.m_indices = q.m_indices; p.num_groups = q.num_groups;
+  p.k_offsets = q.k_offsets;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
   p.nkb = (int)(q.K / BK);
   p.sa_stride = (int)((q.M + q.a_block_rows - 1) / q.a_block_rows);
@@ -574,11 +657,11 @@ hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   p.tiles_m = GROUPED ? (int)(q.M / 128) : (int)((q.M + 255) / 256);
   p.tiles_n = (int)((q.N + BN - 1) / BN);
   p.group_m = 4;
-  const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+  const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n) * (KG ? (unsigned)q.num_groups : 1u);
   if (RING)
     hipLaunchKernelGGL((gemm_ring_kernel<A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_tiled_kernel<256, A_BLK, GROUPED, E8>), dim3(grid), dim3(512), 0,
+    hipLaunchKernelGGL((gemm_tiled_kernel<256, A_BLK, GROUPED, E8, KG>), dim3(grid), dim3(512), 0,
                        stream, p);
   return hipGetLastError();
 }
@@ -593,7 +676,9 @@ hipError_t launch_gemm_tiled(const GemmProblem& q, bool grouped, hipStream_t str
     const char* e = getenv("DG_TILED");
     return e ? (e[0] == 'p' ? 1 : (e[0] == 'r' ? 2 : 0)) : 0;
   }();
-  const bool ring = forced ? forced == 2 : grouped;
+  // (the ring kernel has no epilogue: a dense call with one stays on the pair kernel)
+  const bool plain = q.epi.act == EPI_NONE && q.epi.res == nullptr;
+  const bool ring = (forced ? forced == 2 : grouped) && (grouped || plain);
   if (grouped) {
     if (ring)
       return q.a_block_rows == 1 ? launch_one<true, 1, true>(q, stream)
@@ -606,6 +691,11 @@ hipError_t launch_gemm_tiled(const GemmProblem& q, bool grouped, hipStream_t str
                                : launch_one<true, 128, false>(q, stream);
   return q.a_block_rows == 1 ? launch_one<false, 1, false>(q, stream)
                              : launch_one<false, 128, false>(q, stream);
+}
+
+hipError_t launch_gemm_tiled_kgrouped(const GemmProblem& q, hipStream_t stream) {
+  return q.a_block_rows == 1 ? launch_one<false, 1, false, false, true>(q, stream)
+                             : launch_one<false, 128, false, false, true>(q, stream);
 }
 
 hipError_t launch_gemm_tiled_ue8m0(const GemmProblem& q, hipStream_t stream) {

@@ -194,6 +194,58 @@ int dg_fp8_gemm_nt_epilogue(uint16_t *c, const uint8_t *a, const uint8_t *b,
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Byte transpose of an FP8 (or any 1-byte) matrix [D s3.1: the TN, NN and
+ * TT layouts take operands stored M- or N-major]:
+ *   out[c][r] = in[r][c]; in [rows][cols], out [cols][rows], both 16-byte
+ *   aligned, not overlapping (else DG_ERR_UNSUPPORTED).
+ * Requirements: rows, cols >= 16 and multiples of 16; rows <= 65535 * 128.
+ */
+int dg_transpose_fp8(uint8_t *out, const uint8_t *in, int64_t rows, int64_t cols, void *stream);
+
+/*
+ * GEMM in any of the four operand layouts [D s3.1: NT, TN, NN, TT], with the
+ * scales of dg_fp8_gemm_nt (they describe the logical blocks, whatever the
+ * storage order):
+ *   C[M][N] = A . B^T as in dg_fp8_gemm_nt, where
+ *     layout DG_LAYOUT_NT: a [M][K], b [N][K]   (dg_fp8_gemm_nt itself)
+ *            DG_LAYOUT_TN: a [K][M], b [K][N]
+ *            DG_LAYOUT_NN: a [M][K], b [K][N]
+ *            DG_LAYOUT_TT: a [K][M], b [N][K]
+ * Operands stored M- or N-major are first transposed into the workspace
+ * (dg_transpose_fp8), then the NT kernels run.  workspace_bytes must be at
+ * least dg_fp8_gemm_workspace_bytes(M, N, K, layout) minus the optional
+ * split-K part (the transposed copies are required: DG_ERR_WORKSPACE
+ * otherwise); whatever is left serves the small-M split-K plan.
+ * Requirements: those of dg_fp8_gemm_nt; M % 16 == 0 when A is [K][M],
+ * N % 16 == 0 when B is [K][N]; unknown layout -> DG_ERR_UNSUPPORTED.
+ */
+enum { DG_LAYOUT_NT = 0, DG_LAYOUT_TN = 1, DG_LAYOUT_NN = 2, DG_LAYOUT_TT = 3 };
+size_t dg_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout);
+int dg_fp8_gemm(uint16_t *c, const uint8_t *a, const uint8_t *b, const float *sa, const float *sb,
+                int a_block_rows, int64_t M, int64_t N, int64_t K, int layout,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * K-grouped GEMM [D s3.2: grouped GEMM along the K axis, the MoE
+ * weight-gradient layout]: group g covers K columns
+ * [k_offsets[g], k_offsets[g+1]) and writes its own output
+ *   C[g][m][n] = bf16( sum over the group's K blocks kb of
+ *                      sa(m,kb) * sb(n,kb) * sum_{k in kb} A[m][k] * B[n][k] )
+ *   a [M][K], b [N][K] (K-major; transpose first with dg_transpose_fp8),
+ *   sa, sb over the whole K as in dg_fp8_gemm_nt,
+ *   k_offsets : DEVICE int64 [num_groups + 1], 8-byte aligned, multiples of
+ *               128 with 0 <= k_offsets[g] <= k_offsets[g+1] <= K (an empty
+ *               group writes zeros; values outside the contract give
+ *               unspecified results but no access outside the operands),
+ *   c : out, BF16 [num_groups][M][N].
+ * Requirements: those of dg_fp8_gemm_nt; num_groups >= 1.  Every shape runs
+ * the 256 x 256 tile kernel.
+ */
+int dg_fp8_grouped_gemm_k(uint16_t *c, const uint8_t *a, const uint8_t *b, const float *sa,
+                          const float *sb, int a_block_rows, const int64_t *k_offsets,
+                          int num_groups, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
  * Grouped GEMM, experts contiguous along M [D s2.3, s3.2, s3.3]:
  *   a         : E4M3 [M][K]; the rows of each expert are contiguous, experts
  *               in ascending id, each group padded to a multiple of 128 rows.

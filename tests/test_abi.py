@@ -28,7 +28,9 @@ def test_header_declares_the_boundary():
     for need in ("dg_quantize_fp8_block", "dg_fp8_gemm_nt", "dg_fp8_grouped_gemm_contig",
                  "dg_abi_version", "dg_status_string", "dg_fp8_gemm_nt_workspace_bytes",
                  "dg_get_mk_alignment_for_contiguous_layout", "dg_fp8_gemm_nt_fused_a",
-                 "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_fp8_gemm_nt_epilogue"):
+                 "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_fp8_gemm_nt_epilogue",
+                 "dg_transpose_fp8", "dg_fp8_gemm", "dg_fp8_gemm_workspace_bytes",
+                 "dg_fp8_grouped_gemm_k"):
         assert need in names
 
 
@@ -165,3 +167,30 @@ def test_epilogue_validation(dg):
     assert ge(res=P1) == 4
     assert ge(c=None) == 1
     assert ge(N=260) == 2
+
+
+def test_layouts_transpose_and_k_grouped_validation(dg):
+    lib = dg.lib
+    assert lib.dg_transpose_fp8(None, P, 16, 16, None) == 1
+    assert lib.dg_transpose_fp8(ctypes.c_void_p(0x20000), P, 24, 16, None) == 2
+    assert lib.dg_transpose_fp8(ctypes.c_void_p(0x20000), P1, 16, 16, None) == 4
+    assert lib.dg_transpose_fp8(P, ctypes.c_void_p(0x10010), 64, 64, None) == 3   # overlap
+
+    def gl(layout=1, ws=None, wsb=0, M=256, N=256, K=256):
+        return lib.dg_fp8_gemm(P, P, P, P, P, 128, M, N, K, layout, ws, wsb, None)
+    assert gl(layout=4) == 3 and gl(layout=-1) == 3
+    need = dg.dg_fp8_gemm_workspace_bytes(256, 256, 256, "tn")
+    assert need >= 2 * 256 * 256
+    assert gl() == 5                                   # transposed operands need a workspace
+    assert gl(ws=P, wsb=16) == 5
+    assert gl(ws=P1, wsb=need) == 4
+    assert gl(M=264, ws=P, wsb=1 << 30) == 2            # A given [K][M] needs M % 16 == 0
+    assert dg.dg_fp8_gemm_workspace_bytes(256, 256, 256, "nt") == \
+        dg.dg_fp8_gemm_nt_workspace_bytes(256, 256, 256)
+
+    def gk(ko=P, G=2, M=256, N=256, K=256):
+        return lib.dg_fp8_grouped_gemm_k(P, P, P, P, P, 128, ko, G, M, N, K, None)
+    assert gk(ko=None) == 1
+    assert gk(G=0) == 3
+    assert gk(ko=ctypes.c_void_p(0x10004)) == 4
+    assert gk(K=200) == 2
