@@ -55,7 +55,7 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
 CSRC = os.path.join(ROOT, "fp8_block_scaled_dg_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
-GEMM_TILED_SOURCES = ("gemm_tiled.hip", "dg_device.hpp")
+GEMM_TILED_SOURCES = ("gemm_tiled.hip", "dg_device.hpp", "dg_internal.hpp")
 
 DENSE = [(4096, 7168, 2048), (4096, 4096, 7168), (8192, 8192, 8192)]
 DECODE = [(m, n, k) for (n, k) in [(24576, 1536), (7168, 16384), (4096, 4096)] for m in (1, 16, 64)]
