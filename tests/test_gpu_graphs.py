@@ -1,0 +1,130 @@
+"""Every entry point captured into a HIP graph: replayed several times, with
+eager launches and synchronisations between the replays and the outputs
+zeroed before each, a graph must reproduce the eager result bit for bit.
+The calls enqueue kernels only (no memsets), and the split-K counters are
+left zeroed by every call, which this exercises across replays."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from gpu_util import dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dg():
+    need_gpu()
+    import fp8_block_scaled_dg_amd as m
+    return m
+
+
+def check_graph(make_outputs, run):
+    """run(outs) enqueues the operation writing into the tensors outs."""
+    eager = make_outputs()
+    run(eager)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in eager]
+    sets = [make_outputs() for _ in range(2)]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for outs in sets:
+                run(outs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for outs in sets:
+            for t in outs:
+                t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for outs in sets:
+            for t, e in zip(outs, eager):
+                assert torch.equal(t.view(torch.uint8), e.view(torch.uint8)), "replay %d" % rep
+        again = make_outputs()                      # eager work between replays
+        run(again)
+        torch.cuda.synchronize()
+        for t, e in zip(again, eager):
+            assert torch.equal(t.view(torch.uint8), e.view(torch.uint8))
+
+
+def bf16(M, N):
+    return lambda: [torch.empty((M, N), dtype=torch.bfloat16, device="cuda")]
+
+
+def quantised(orc, M, N, K, br=1, seed=0):
+    qa, sa = orc.quantize(datagen.normal((M, K), 1.0, seed=seed, stream=0), br)
+    qb, sb = orc.quantize(datagen.normal((N, K), 0.02, seed=seed, stream=1), 128)
+    return dev(qa), dev(sa), dev(qb), dev(sb)
+
+
+@pytest.mark.parametrize("br", [128, 1])
+def test_graph_quantisers(dg, br):
+    x = dev(datagen.normal((300, 1152), 1.0, seed=2))
+    nkb, nrb = 9, -(-300 // br)
+
+    def outs():
+        return [torch.empty((300, 1152), dtype=torch.uint8, device="cuda"),
+                torch.empty((nkb, nrb), dtype=torch.float32, device="cuda"),
+                torch.empty((300, 1152), dtype=torch.uint8, device="cuda"),
+                torch.empty((3, nrb), dtype=torch.int32, device="cuda")]
+
+    def run(o):
+        dg.dg_quantize_fp8_block(o[0], o[1], x, br)
+        dg.dg_quantize_fp8_block_ue8m0(o[2], o[3], x, br)
+    check_graph(outs, run)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (1, 24576, 1536), (8, 1032, 1024)])
+def test_graph_fused_activation_quantisation(dg, orc, M, N, K):
+    a = dev(datagen.normal((M, K), 1.0, seed=3, stream=0))
+    _, _, qb, sb = quantised(orc, 1, N, K)
+    wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    check_graph(bf16(M, N), lambda o: dg.dg_fp8_gemm_nt_fused_a(o[0], a, qb, sb, workspace=ws))
+
+
+@pytest.mark.parametrize("M,N,K,act", [(300, 520, 640, "swiglu"), (12, 2056, 16384, "silu"),
+                                       (4, 1032, 1024, "gelu")])
+def test_graph_epilogue_with_residual(dg, orc, M, N, K, act):
+    qa, sa, qb, sb = quantised(orc, M, N, K, seed=4)
+    n_out = N // 2 if act == "swiglu" else N
+    r = dev(datagen.normal((M, n_out), 1.0, seed=5)).to(torch.bfloat16)
+    wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    check_graph(bf16(M, n_out), lambda o: dg.dg_fp8_gemm_nt_epilogue(
+        o[0], qa, qb, sa, sb, 1, act=act, residual=r, workspace=ws))
+
+
+def test_graph_ue8m0_gemm(dg, orc):
+    M, N, K = 512, 768, 1024
+    qa, ea = orc.quantize_ue8m0(datagen.normal((M, K), 1.0, seed=6, stream=0), 1)
+    qb, eb = orc.quantize_ue8m0(datagen.normal((N, K), 0.02, seed=6, stream=1), 128)
+    a, b = dev(qa), dev(qb)
+    sfa, sfb = dev(orc.pack_ue8m0(ea)), dev(orc.pack_ue8m0(eb))
+    check_graph(bf16(M, N), lambda o: dg.dg_fp8_gemm_nt_ue8m0(o[0], a, b, sfa, sfb, 1))
+
+
+@pytest.mark.parametrize("layout", ["tn", "nn", "tt"])
+def test_graph_layouts(dg, orc, layout):
+    M, N, K = 256, 384, 512
+    qa, sa = orc.quantize(datagen.normal((M, K), 1.0, seed=7, stream=0), 1)
+    qb, sb = orc.quantize(datagen.normal((N, K), 0.02, seed=7, stream=1), 128)
+    a = dev(np.ascontiguousarray(qa.T) if layout in ("tn", "tt") else qa)
+    b = dev(np.ascontiguousarray(qb.T) if layout in ("tn", "nn") else qb)
+    sa_d, sb_d = dev(sa), dev(sb)
+    ws = torch.empty(dg.dg_fp8_gemm_workspace_bytes(M, N, K, layout), dtype=torch.uint8,
+                     device="cuda")
+    check_graph(bf16(M, N), lambda o: dg.dg_fp8_gemm(o[0], a, b, sa_d, sb_d, 1, layout=layout,
+                                                     workspace=ws))
+
+
+def test_graph_k_grouped(dg, orc):
+    M, N, K = 300, 520, 1664
+    qa, sa, qb, sb = quantised(orc, M, N, K, seed=8)
+    ko = torch.tensor([0, 384, 384, 1024, 1664], dtype=torch.int64, device="cuda")
+    check_graph(lambda: [torch.empty((4, M, N), dtype=torch.bfloat16, device="cuda")],
+                lambda o: dg.dg_fp8_grouped_gemm_k(o[0], qa, qb, sa, sb, 1, ko))
