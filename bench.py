@@ -352,7 +352,13 @@ class Decode:
             sb = torch.rand((copies, K // 128, N // 128), device="cuda", generator=g) * 1e-3
             a = torch.from_numpy(datagen.normal((M, K), 1.0, seed=seed, stream=M)).cuda()
             ws_bytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-            self.items.append(dict(
+            # power-of-two (UE8M0) exponent bytes 120..127, four K blocks per int32
+            w = cdiv(K // 128, 4)
+            sfa = (torch.randint(120, 128, (w, M, 4), device="cuda", generator=g)
+                   .to(torch.uint8).view(torch.int32).reshape(w, M))
+            sfb = (torch.randint(120, 128, (w, cdiv(N, 128), 4), device="cuda", generator=g)
+                   .to(torch.uint8).view(torch.int32).reshape(w, cdiv(N, 128)))
+            self.items.append(dict(sfa=sfa, sfb=sfb,
                 M=M, N=N, K=K, qb=qb, sb=sb, a=a, copies=copies,
                 qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
                 sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
@@ -397,6 +403,11 @@ class Decode:
         return timer.time(lambda: [self.gemm(it, i) for i in range(rot)], reps,
                           key=("dec", n)) / rot
 
+    def gemm_e8(self, it, i):
+        j = i % it["copies"]
+        self.dg.dg_fp8_gemm_nt_ue8m0(it["c"], it["qa"], it["qb"][j], it["sfa"], it["sfb"], 1,
+                                     workspace=it["ws"])
+
     def quantise_and_gemm(self, it, i):
         self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
         self.gemm(it, i)
@@ -421,6 +432,9 @@ class Decode:
             if it["M"] <= self.dg.FUSED_A_MAX_M:
                 row["fused_us"] = timer.time(lambda: [self.fused(it, i) for i in range(rot)],
                                              reps, key=("decf", n)) / rot * 1e3
+            # the same GEMM with power-of-two (UE8M0) scales on the scaled MFMA
+            row["ue8m0_gemm_us"] = timer.time(lambda: [self.gemm_e8(it, i) for i in range(rot)],
+                                              reps, key=("dece", n)) / rot * 1e3
             out.append(row)
         return out
 

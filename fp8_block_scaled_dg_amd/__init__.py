@@ -54,7 +54,8 @@ def _load():
     lib.dg_quantize_fp8_block_ue8m0.restype = i32
     lib.dg_quantize_fp8_block_ue8m0.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     lib.dg_fp8_gemm_nt_ue8m0.restype = i32
-    lib.dg_fp8_gemm_nt_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    lib.dg_fp8_gemm_nt_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp,
+                                         ctypes.c_size_t, vp]
     lib.dg_fp8_gemm_nt_epilogue.restype = i32
     lib.dg_fp8_gemm_nt_epilogue.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, vp, vp,
                                             ctypes.c_size_t, vp]
@@ -202,7 +203,8 @@ def dg_quantize_fp8_block_ue8m0(q, sf, x, block_rows: int = 128, stream=None) ->
                                            _stream(stream)), "dg_quantize_fp8_block_ue8m0")
 
 
-def dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, a_block_rows: int = 128, stream=None) -> None:
+def dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, a_block_rows: int = 128, workspace=None,
+                         stream=None) -> None:
     """C[M,N] (bf16) = A[M,K] . B[N,K]^T with packed UE8M0 block scales."""
     c = _bf16(c, "c")
     a = _codes(a, "a")
@@ -219,7 +221,8 @@ def dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, a_block_rows: int = 128, stream=None
     if sfb.numel() != cdiv(cdiv(K, 128), 4) * cdiv(N, 128):
         raise ValueError("sfb must hold ceil(K/512)*ceil(N/128) int32")
     _check(lib.dg_fp8_gemm_nt_ue8m0(_ptr(c), _ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb), a_block_rows,
-                                    M, N, K, _stream(stream)), "dg_fp8_gemm_nt_ue8m0")
+                                    M, N, K, _ptr(workspace), _workspace_bytes(workspace),
+                                    _stream(stream)), "dg_fp8_gemm_nt_ue8m0")
 
 
 FUSED_A_MAX_M = 16

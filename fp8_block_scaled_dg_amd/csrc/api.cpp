@@ -142,18 +142,25 @@ int dg_fp8_gemm_nt_epilogue(uint16_t* c, const uint8_t* a, const uint8_t* b, con
 
 int dg_fp8_gemm_nt_ue8m0(uint16_t* c, const uint8_t* a, const uint8_t* b, const int32_t* sfa,
                          const int32_t* sfb, int a_block_rows, int64_t M, int64_t N, int64_t K,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
   // the FP32-scale checks apply unchanged (the scale pointers only need
   // 4-byte alignment in both forms)
   int st = check_gemm(c, a, b, reinterpret_cast<const float*>(sfa),
                       reinterpret_cast<const float*>(sfb), a_block_rows, M, N, K);
   if (st != DG_OK) return st;
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles > INT32_MAX) return DG_ERR_SHAPE;
+  st = check_workspace(M, N, K, &workspace, &workspace_bytes);
+  if (st != DG_OK) return st;
   dg::GemmProblem p{c, a, b, nullptr, nullptr, nullptr, 1, a_block_rows, M, N, K};
   p.sfa = reinterpret_cast<const uint32_t*>(sfa);
   p.sfb = reinterpret_cast<const uint32_t*>(sfb);
-  return from_hip(dg::launch_gemm_tiled_ue8m0(p, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dg::skinny_applies(M, N, K)) {
+    if (dg::stream_preferred(M, N, K)) return from_hip(dg::launch_gemm_stream(p, s));
+    return from_hip(dg::launch_gemm_skinny(p, workspace, workspace_bytes, s));
+  }
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles > INT32_MAX) return DG_ERR_SHAPE;
+  return from_hip(dg::launch_gemm_tiled_ue8m0(p, s));
 }
 
 int dg_fp8_gemm_nt_fused_a(uint16_t* c, const float* a, const uint8_t* b, const float* sb,

@@ -50,6 +50,8 @@ struct SkinnyArgs {
   Epilogue epi;
   const uint8_t* a;
   const float* af;  // FP32 A when the kernel quantises A itself, else null
+  const uint32_t* sfa;  // E8: packed UE8M0 exponents (four K blocks per word)
+  const uint32_t* sfb;
   const uint8_t* b;
   const float* sa;
   const float* sb;
@@ -83,9 +85,14 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
 // MFMAs.  FP32 A is staged through LDS rather than registers: the compiler
 // waits for every load in flight before using a register loaded ahead of LDS
 // DMA instructions, which would drain the ring each step.
-template <int MP, int F, bool AF32 = false>
+// E8: power-of-two (UE8M0) scales (DeepGEMM page on pzsr.cn, s3.1): the
+// stages carry the packed exponent words in place of the FP32 scales, the
+// scaled MFMA applies them and the accumulators chain through K; UE8M0 has
+// no zero, so the steps past the K range zero their B fragment instead.
+template <int MP, int F, bool AF32 = false, bool E8 = false>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   static_assert(!AF32 || MP == 16, "in-kernel quantisation covers up to 16 rows");
+  static_assert(!(AF32 && E8), "in-kernel quantisation uses FP32 scales");
   constexpr int BNT = 64 * F;                     // B rows per workgroup (F fragments per wave)
   constexpr int MPE = MP < 32 ? 32 : MP;          // A rows staged (>= 4 DMA instructions)
   constexpr int B_BYTES = BNT * BK;               // 8 or 16 KB
@@ -163,11 +170,15 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
         __builtin_amdgcn_global_load_lds((const void*)(p.a + aoff[j] + (uint32_t)kb * BK),
                                          (__attribute__((address_space(3))) void*)(st + B_BYTES + (j * 4 + wave) * 1024),
                                          16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(p.sa + (int64_t)kb * p.sa_stride + sa_row),
+      const void* sa_src = E8 ? (const void*)(p.sfa + (int64_t)(kb >> 2) * p.sa_stride + sa_row)
+                              : (const void*)(p.sa + (int64_t)kb * p.sa_stride + sa_row);
+      __builtin_amdgcn_global_load_lds(sa_src,
                                        (__attribute__((address_space(3))) void*)(st + B_BYTES + A_BYTES + wave * 256),
                                        4, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((const void*)(p.sb + (int64_t)kb * p.sb_stride + nb),
+    const void* sb_src = E8 ? (const void*)(p.sfb + (int64_t)(kb >> 2) * p.sb_stride + nb)
+                            : (const void*)(p.sb + (int64_t)kb * p.sb_stride + nb);
+    __builtin_amdgcn_global_load_lds(sb_src,
                                      (__attribute__((address_space(3))) void*)(st + B_BYTES + A_BYTES + SA_BYTES + wave * 256),
                                      4, 0, 0);
   };
@@ -237,24 +248,39 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     // three) re-read the last staged block with a zero scale: they add exactly
     // 0, and they keep the loop free of branches, without which the
     // compiler's LDS-DMA tracking falls back to waiting for every load.
-    const float sbv_l = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64];
-    const float sbv = it < nk ? sbv_l : 0.0f;
     float s[NI];
-    const float* sa_l = AF32 ? reinterpret_cast<const float*>(qb + 16 * BK)
-                             : reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
+    int ea[NI], eb = 0;  // E8: exponent bytes of this stage's K block
+    if constexpr (E8) {
+      const int sh = 8 * ((kb0 + (it < nk ? it : nk - 1)) & 3);
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(cur + B_BYTES + A_BYTES);
+      eb = (int)((w[SA_BYTES / 4 + wave * 64] >> sh) & 0xFFu);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) s[i] = sa_l[16 * i + fr] * sbv;  // (all 64 slots equal for 128-row A blocks)
+      for (int i = 0; i < NI; ++i) ea[i] = (int)((w[wave * 64 + 16 * i + fr] >> sh) & 0xFFu);
+    } else {
+      const float sbv_l = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64];
+      const float sbv = it < nk ? sbv_l : 0.0f;
+      const float* sa_l = AF32 ? reinterpret_cast<const float*>(qb + 16 * BK)
+                               : reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) s[i] = sa_l[16 * i + fr] * sbv;  // (all 64 slots equal for 128-row A blocks)
+    }
     v8i af[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) af[i] = read_frag(AF32 ? qb : cur + B_BYTES, 16 * i, off0, off1);
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-      const v8i bf = read_frag(cur, wave * 16 * F + 16 * f, off0, off1);
+      v8i bf = read_frag(cur, wave * 16 * F + 16 * f, off0, off1);
+      if constexpr (E8) bf &= (it < nk ? -1 : 0);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const v4f part =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 0, 0, 0);
-        acc[f][i] += part * s[i];
+        if constexpr (E8) {
+          acc[f][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], acc[f][i], 0, 0,
+                                                                       0, eb, 0, ea[i]);
+        } else {
+          const v4f part =
+              __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[i], zero, 0, 0, 0, 0, 0, 0);
+          acc[f][i] += part * s[i];
+        }
       }
     }
   };
@@ -448,6 +474,7 @@ hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, voi
                                       size_t workspace_bytes, hipStream_t stream) {
   SkinnyArgs p;
   p.c = q.c; p.a = nullptr; p.af = af; p.b = q.b; p.sa = nullptr; p.sb = q.sb;
+  p.sfa = nullptr; p.sfb = nullptr;
   p.epi = resolved_epilogue(q);
   p.a_block_rows = 1;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
@@ -469,10 +496,31 @@ hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, voi
   return hipGetLastError();
 }
 
+template <bool E8>
+hipError_t launch_mp(const SkinnyArgs& p, int bn, int64_t M, unsigned grid, hipStream_t stream) {
+  if (bn == 64) {
+    if (M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 1, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+    else if (M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 1, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 1, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+  } else {
+    if (M <= 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 2, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+    else if (M <= 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 2, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 2, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
   SkinnyArgs p;
   p.c = q.c; p.a = q.a; p.af = nullptr; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.sfa = q.sfa; p.sfb = q.sfb;
   p.epi = resolved_epilogue(q);
   p.a_block_rows = q.a_block_rows;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;
@@ -485,22 +533,8 @@ hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t work
   p.partials = static_cast<float*>(workspace);
   const int bn = choose_bn(q.M, q.N);
   const unsigned grid = (unsigned)(((q.N + bn - 1) / bn) * S);
-  if (bn == 64) {
-    if (q.M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<16, 1>), dim3(grid), dim3(256), 0, stream, p);
-    else if (q.M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<32, 1>), dim3(grid), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((gemm_skinny_kernel<64, 1>), dim3(grid), dim3(256), 0, stream, p);
-  } else {
-    if (q.M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<16, 2>), dim3(grid), dim3(256), 0, stream, p);
-    else if (q.M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<32, 2>), dim3(grid), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((gemm_skinny_kernel<64, 2>), dim3(grid), dim3(256), 0, stream, p);
-  }
-  return hipGetLastError();
+  return q.sfa ? launch_mp<true>(p, bn, q.M, grid, stream)
+               : launch_mp<false>(p, bn, q.M, grid, stream);
 }
 
 }  // namespace dg

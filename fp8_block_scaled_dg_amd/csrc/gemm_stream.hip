@@ -38,6 +38,8 @@ struct StreamArgs {
   const uint8_t* b;
   const float* sa;
   const float* sb;
+  const uint32_t* sfa;  // E8: packed UE8M0 exponents (four K blocks per word)
+  const uint32_t* sfb;
   int a_block_rows;
   int M, N, K;
   int nkb;
@@ -45,7 +47,10 @@ struct StreamArgs {
   int sb_stride;  // ceil(N / 128)
 };
 
-template <int RW, int MP, int KS, int U>
+// E8: power-of-two (UE8M0) scales (DeepGEMM page on pzsr.cn, s3.1) applied
+// by the scaled MFMA, accumulators chained through K.  UE8M0 has no zero, so
+// K blocks past a wave's range zero their B fragment instead of the scale.
+template <int RW, int MP, int KS, int U, bool E8 = false>
 __global__ void __launch_bounds__(256) gemm_stream_kernel(StreamArgs p) {
   constexpr int NF = RW / 16;  // B fragments per wave
   constexpr int NI = MP / 16;  // A fragments
@@ -92,6 +97,8 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(StreamArgs p) {
     v8i a[U][NI];
     float sa[U][NI];
     float sb[U];
+    int ea[U][NI];  // E8: exponent bytes
+    int eb[U];
   };
 
   // K blocks past this wave's range re-load its last block with a zero scale
@@ -106,16 +113,25 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(StreamArgs p) {
         const v4i lo = *reinterpret_cast<const v4i*>(bp[f] + ko);
         const v4i hi = *reinterpret_cast<const v4i*>(bp[f] + ko + 16);
         x.b[u][f] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (E8) x.b[u][f] &= (in ? -1 : 0);
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const v4i lo = *reinterpret_cast<const v4i*>(ap[i] + ko);
         const v4i hi = *reinterpret_cast<const v4i*>(ap[i] + ko + 16);
         x.a[u][i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        x.sa[u][i] = p.sa[(int64_t)kb * p.sa_stride + sa_col[i]] * aval[i];
+        if constexpr (E8)
+          x.ea[u][i] = (int)((p.sfa[(int64_t)(kb >> 2) * p.sa_stride + sa_col[i]] >>
+                              (8 * (kb & 3))) & 0xFFu);
+        else
+          x.sa[u][i] = p.sa[(int64_t)kb * p.sa_stride + sa_col[i]] * aval[i];
       }
-      const float sbv = p.sb[(int64_t)kb * p.sb_stride + nb];
-      x.sb[u] = in ? sbv : 0.0f;
+      if constexpr (E8) {
+        x.eb[u] = (int)((p.sfb[(int64_t)(kb >> 2) * p.sb_stride + nb] >> (8 * (kb & 3))) & 0xFFu);
+      } else {
+        const float sbv = p.sb[(int64_t)kb * p.sb_stride + nb];
+        x.sb[u] = in ? sbv : 0.0f;
+      }
     }
   };
 
@@ -133,9 +149,14 @@ __global__ void __launch_bounds__(256) gemm_stream_kernel(StreamArgs p) {
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x.b[u][f], x.a[u][i],
-                                                                            zero, 0, 0, 0, 0, 0, 0);
-          acc[f][i] += part * (x.sa[u][i] * x.sb[u]);
+          if constexpr (E8) {
+            acc[f][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                x.b[u][f], x.a[u][i], acc[f][i], 0, 0, 0, x.eb[u], 0, x.ea[u][i]);
+          } else {
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                x.b[u][f], x.a[u][i], zero, 0, 0, 0, 0, 0, 0);
+            acc[f][i] += part * (x.sa[u][i] * x.sb[u]);
+          }
         }
   };
 
@@ -200,7 +221,11 @@ hipError_t launch(const StreamArgs& p, hipStream_t stream) {
   constexpr int SPW = 4 / KS;
   const int strips = (p.N + RW - 1) / RW;
   const unsigned grid = (unsigned)((strips + SPW - 1) / SPW);
-  hipLaunchKernelGGL((gemm_stream_kernel<RW, MP, KS, U>), dim3(grid), dim3(256), 0, stream, p);
+  if (p.sfa)
+    hipLaunchKernelGGL((gemm_stream_kernel<RW, MP, KS, U, true>), dim3(grid), dim3(256), 0, stream,
+                       p);
+  else
+    hipLaunchKernelGGL((gemm_stream_kernel<RW, MP, KS, U>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -245,6 +270,7 @@ bool stream_preferred(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_stream(const GemmProblem& q, hipStream_t stream) {
   StreamArgs p;
   p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.sfa = q.sfa; p.sfb = q.sfb;
   p.epi = resolved_epilogue(q);
   p.a_block_rows = q.a_block_rows;
   p.M = (int)q.M; p.N = (int)q.N; p.K = (int)q.K;

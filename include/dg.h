@@ -132,12 +132,15 @@ int dg_fp8_gemm_nt(uint16_t *c, const uint8_t *a, const uint8_t *b,
  *   c, a, b, a_block_rows, M, N, K and their requirements: as dg_fp8_gemm_nt.
  *   sfa : int32 [ceil(K/512)][ceil(M/a_block_rows)], packed as written by
  *         dg_quantize_fp8_block_ue8m0; sfb : int32 [ceil(K/512)][ceil(N/128)].
- * Every shape runs the 256 x 256 tile kernel (no small-M plan).
+ *   workspace / workspace_bytes: optional split-K scratch for M <= 64, as
+ *         for dg_fp8_gemm_nt (same size query, same counter rule).
+ * The kernel plan is dg_fp8_gemm_nt's (small-M kernels for M <= 64).
  * Deterministic.
  */
 int dg_fp8_gemm_nt_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
                          const int32_t *sfa, const int32_t *sfb, int a_block_rows,
-                         int64_t M, int64_t N, int64_t K, void *stream);
+                         int64_t M, int64_t N, int64_t K,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * NT GEMM of FP32 activations with FP8 weights, the activations quantised

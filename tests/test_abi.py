@@ -146,7 +146,7 @@ def test_ue8m0_validation(dg):
                                            None) == 4
 
     def ge(c=P, a=P, b=P, sfa=P, sfb=P, br=128, M=256, N=256, K=256):
-        return lib.dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, br, M, N, K, None)
+        return lib.dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, br, M, N, K, None, 0, None)
     for kw in ("c", "a", "b", "sfa", "sfb"):
         assert ge(**{kw: None}) == 1
     assert ge(br=2) == 3

@@ -165,3 +165,48 @@ def test_end_to_end_ue8m0_and_determinism(dg, orc):
     oqb, oeb = orc.quantize_ue8m0(b, 128)
     ref = orc.gemm_nt(oqa, orc.ue8m0_scales(oea), oqb, orc.ue8m0_scales(oeb), a_block_rows=1)
     assert_close(bf16_to_f64(outs[0]), ref, what="ue8m0 end to end")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 512), (5, 2056, 1024), (16, 136, 2048), (33, 1000, 640),
+                                   (64, 384, 4096), (2, 24576, 384), (16, 2056, 16384),
+                                   (12, 16392, 384)])
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_gemm_ue8m0_small_m(dg, orc, M, N, K, use_ws):
+    """The small-M kernels with power-of-two scales (the streaming kernel, the
+    LDS-ring kernel with and without split-K), ragged N, K ranges that split
+    unevenly: compared with the oracle in full."""
+    qa, ea, qb, eb = operands(orc, M, N, K, 1, seed=M * 5 + N)
+    ws = None
+    if use_ws:
+        nb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm_nt_ue8m0(c, dev(qa), dev(qb), dev(orc.pack_ue8m0(ea)), dev(orc.pack_ue8m0(eb)),
+                            1, workspace=ws)
+    torch.cuda.synchronize()
+    ref = orc.gemm_nt(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), a_block_rows=1)
+    assert_close(bf16_to_f64(c), ref, what="ue8m0 small-M %dx%dx%d ws=%s" % (M, N, K, use_ws))
+
+
+def test_gemm_ue8m0_small_m_extreme_exponents(dg, orc):
+    """Exponent bytes near both ends of the range on the small-M paths: the K
+    steps past a split's range must add nothing even where 2^(Ea+Eb-254)
+    is large (they zero an operand, as UE8M0 has no zero scale)."""
+    for (M, N, K) in [(4, 1032, 1280), (16, 4104, 8320), (40, 1032, 640)]:
+        g = np.random.default_rng(M + N)
+        codes = np.array([0x00, 0x38, 0xB8, 0x40, 0xC0], np.uint8)
+        qa = codes[g.integers(0, 5, (M, K))]
+        qb = codes[g.integers(0, 5, (N, K))]
+        ea = g.integers(150, 160, (K // 128, M)).astype(np.uint8)
+        eb = g.integers(100, 110, (K // 128, -(-N // 128))).astype(np.uint8)
+        for use_ws in (False, True):
+            ws = None
+            if use_ws:
+                nb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+                ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+            c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            dg.dg_fp8_gemm_nt_ue8m0(c, dev(qa), dev(qb), dev(orc.pack_ue8m0(ea)),
+                                    dev(orc.pack_ue8m0(eb)), 1, workspace=ws)
+            torch.cuda.synchronize()
+            ref = orc.gemm_nt(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), a_block_rows=1)
+            assert_close(bf16_to_f64(c), ref, what="ue8m0 extreme %dx%dx%d" % (M, N, K))
