@@ -168,6 +168,31 @@ struct IntTag {
   static constexpr int value = V;
 };
 
+// f(IntTag<0>{}) ... f(IntTag<N-1>{}), unrolled at compile time.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F&& f) {
+  if constexpr (I < N) {
+    f(IntTag<I>{});
+    static_for_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_from<0, N>(f);
+}
+
+// As static_for, but stops after the first call that returns false.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_while_from(F&& f) {
+  if constexpr (I < N) {
+    if (f(IntTag<I>{})) static_while_from<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_while(F&& f) {
+  static_while_from<0, N>(f);
+}
+
 // The results t[0..3] of columns n .. n+3 (n % 4 == 0) of row m after the
 // epilogue ACT (an EpiAct; SwiGLU pairs the columns: 2j gate, 2j+1 up ->
 // output column j), then the residual if RES, then BF16 round-to-nearest-

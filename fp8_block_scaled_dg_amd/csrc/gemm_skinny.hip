@@ -39,7 +39,7 @@ namespace {
 
 constexpr int BN = 128;
 constexpr int BK = 128;
-constexpr int NS = 3;              // LDS ring depth (<= 75 KB: two workgroups per CU)
+constexpr int kMaxNS = 8;          // deepest LDS ring (named slot arrays l0 .. l7)
 constexpr int kMaxCounters = 8192; // tiles: N up to 1M with 128-row tiles
 constexpr int kMaxSplits = 16;
 
@@ -87,9 +87,12 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
 // DMA instructions, which would drain the ring each step.
 // E8: power-of-two (UE8M0) scales (DeepGEMM page on pzsr.cn, s3.1): the
 // stages carry the packed exponent words in place of the FP32 scales, the
-// scaled MFMA applies them and the accumulators chain through K; UE8M0 has
-// no zero, so the steps past the K range zero their B fragment instead.
-template <int MP, int F, bool AF32 = false, bool E8 = false>
+// scaled MFMA applies them and the accumulators chain through K.
+// NS: LDS ring depth; NS - 1 stages are in flight while one is consumed.
+// Measured on MI355X over the nine decode shapes: 4 or 6 slots (one
+// workgroup per CU) are no faster than 3 at the best split count, so the
+// launches use 3.
+template <int MP, int F, bool AF32 = false, bool E8 = false, int NS = 3>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   static_assert(!AF32 || MP == 16, "in-kernel quantisation covers up to 16 rows");
   static_assert(!(AF32 && E8), "in-kernel quantisation uses FP32 scales");
@@ -104,10 +107,17 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   constexpr int A_IT = A_BYTES / 1024 / 4;
   constexpr int PER_STAGE = B_IT + A_IT + (AF32 ? 1 : 2);  // + the A scale row + the B scale
   constexpr int NI = MP / 16;                     // A fragments
-  static_assert(NS == 3, "the ring below is written out for three slots");
+  static_assert(NS >= 3 && NS <= kMaxNS, "ring depth");
+  static_assert((NS - 2) * PER_STAGE <= 63, "s_waitcnt vmcnt range");
+  static_assert(NS * STAGE + (AF32 ? 16 * BK + 16 * 4 : 0) <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t l0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t l1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t l2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t l3[NS > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t l4[NS > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t l5[NS > 5 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t l6[NS > 6 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t l7[NS > 7 ? STAGE : 16];
   // AF32 code buffer: 16 rows x 128 codes, then the 16 row scales (never a
   // DMA target, so stores to it need no wait on the DMA in flight)
   __shared__ __attribute__((aligned(128))) uint8_t qb[AF32 ? 16 * BK + 16 * 4 : 16];
@@ -218,8 +228,20 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     for (int i = 0; i < NI; ++i) acc[f][i] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  issue_stage(0, l0);
-  issue_stage(1, l1);
+  // ring slot i (one named array per slot: see above)
+  auto slot = [&](auto tag) -> uint8_t* {
+    constexpr int i = decltype(tag)::value;
+    if constexpr (i == 0) return l0;
+    else if constexpr (i == 1) return l1;
+    else if constexpr (i == 2) return l2;
+    else if constexpr (i == 3) return l3;
+    else if constexpr (i == 4) return l4;
+    else if constexpr (i == 5) return l5;
+    else if constexpr (i == 6) return l6;
+    else return l7;
+  };
+  // stages 0 .. NS-2 go into slots 0 .. NS-2; stage s always lives in slot s % NS
+  static_for<NS - 1>([&](auto tag) { issue_stage(decltype(tag)::value, slot(tag)); });
 
   // one K block: stage `it` sits in `cur`; stage it+NS-1 goes into `nxt`
   // (the slot of stage it-1, free once every wave has passed this barrier)
@@ -244,21 +266,20 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
       asm volatile("s_barrier" ::: "memory");
     }
 
-    // Steps past the K range (the unrolled ring always runs whole rounds of
-    // three) re-read the last staged block with a zero scale: they add exactly
-    // 0, and they keep the loop free of branches, without which the
-    // compiler's LDS-DMA tracking falls back to waiting for every load.
+    // Stages past the K range (issued by the last NS - 1 steps) re-stage the
+    // last block; they are never consumed.  Loads are never branched around:
+    // at such a merge the compiler's LDS-DMA tracking falls back to waiting
+    // for every load.
     float s[NI];
     int ea[NI], eb = 0;  // E8: exponent bytes of this stage's K block
     if constexpr (E8) {
-      const int sh = 8 * ((kb0 + (it < nk ? it : nk - 1)) & 3);
+      const int sh = 8 * ((kb0 + it) & 3);
       const uint32_t* w = reinterpret_cast<const uint32_t*>(cur + B_BYTES + A_BYTES);
       eb = (int)((w[SA_BYTES / 4 + wave * 64] >> sh) & 0xFFu);
 #pragma unroll
       for (int i = 0; i < NI; ++i) ea[i] = (int)((w[wave * 64 + 16 * i + fr] >> sh) & 0xFFu);
     } else {
-      const float sbv_l = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64];
-      const float sbv = it < nk ? sbv_l : 0.0f;
+      const float sbv = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64];
       const float* sa_l = AF32 ? reinterpret_cast<const float*>(qb + 16 * BK)
                                : reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
 #pragma unroll
@@ -269,8 +290,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     for (int i = 0; i < NI; ++i) af[i] = read_frag(AF32 ? qb : cur + B_BYTES, 16 * i, off0, off1);
 #pragma unroll
     for (int f = 0; f < F; ++f) {
-      v8i bf = read_frag(cur, wave * 16 * F + 16 * f, off0, off1);
-      if constexpr (E8) bf &= (it < nk ? -1 : 0);
+      const v8i bf = read_frag(cur, wave * 16 * F + 16 * f, off0, off1);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if constexpr (E8) {
@@ -285,11 +305,23 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     }
   };
 
-  for (int it = 0; it < nk; it += NS) {
-    body(it, l0, l2);
-    body(it + 1, l1, l0);
-    body(it + 2, l2, l1);
+  // whole rounds of NS steps (step it + i reads slot i and refills slot
+  // i - 1), then the last nk % NS steps after the loop: an exit branch inside
+  // the loop body would make the compiler wait for every load at the top of
+  // each round
+  int it = 0;
+  for (; it + NS <= nk; it += NS) {
+    static_for<NS>([&](auto tag) {
+      constexpr int i = decltype(tag)::value;
+      body(it + i, slot(tag), slot(IntTag<(i + NS - 1) % NS>{}));
+    });
   }
+  static_while<NS - 1>([&](auto tag) {
+    constexpr int i = decltype(tag)::value;
+    if (it + i >= nk) return false;
+    body(it + i, slot(tag), slot(IntTag<(i + NS - 1) % NS>{}));
+    return true;
+  });
   // drain the re-staged loads past the range before the workgroup exits
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 

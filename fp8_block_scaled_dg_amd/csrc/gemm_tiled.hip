@@ -469,12 +469,14 @@ gemm_tiled_kernel(TiledArgs p) {
 //
 // A half stage is one 32 KB operand slice (A or B, 256 rows x 128 K bytes);
 // the 160 KB of LDS hold five of them.  Step k reads A_k and B_k from slots
-// 2k mod 5 and 2k+1 mod 5 while the DMA for B_{k+1} and A_{k+2} streams into
-// the two slots that step k-1 released, one DMA instruction per four MFMAs, so
-// every slice is requested one to two steps before it is read.  At the top of
-// step k every slice except the most recent (A_{k+1}) must have landed:
-// s_waitcnt vmcnt(4), then one barrier, which also certifies that all waves
-// have finished reading the slots about to be refilled.
+// 2k+1 mod 5 and 2k mod 5 while the DMA for A_{k+1}, then B_{k+2}, streams
+// into the two slots that step k-1 released, one DMA instruction per four
+// MFMAs.  B (the weights, from HBM) is thus requested about one and a half
+// steps before it is read, A (re-read by many tiles, mostly from L2) about
+// one step before.  At the top of step k every slice except the most recent
+// (B_{k+1}) must have landed: s_waitcnt vmcnt(4), then one barrier, which
+// also certifies that all waves have finished reading the slots about to be
+// refilled.
 template <int A_BLK, bool GROUPED>
 __global__ void __launch_bounds__(512)
 gemm_ring_kernel(TiledArgs p) {
@@ -541,14 +543,14 @@ gemm_ring_kernel(TiledArgs p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) sa_nxt[i] = p.sa[sa_idx[i]];
 
-  // prologue: A_0, B_0, A_1 (A_1 re-reads block 0 when K has one block)
-  lda.issue(p.a, r0, wave, 0);
-  ldb.issue(bbase, r1, wave, 0);
-  lda.issue(p.a, r2, wave, last > 0 ? 1 : 0);
+  // prologue: A_0, B_0, B_1 (B_1 re-reads block 0 when K has one block)
+  lda.issue(p.a, r1, wave, 0);
+  ldb.issue(bbase, r0, wave, 0);
+  ldb.issue(bbase, r2, wave, last > 0 ? 1 : 0);
 
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  auto step = [&](const uint8_t* a_l, const uint8_t* b_l, uint8_t* wb, uint8_t* wa, int kb) {
+  auto step = [&](const uint8_t* a_l, const uint8_t* b_l, uint8_t* wa, uint8_t* wb, int kb) {
     __builtin_amdgcn_s_waitcnt(kVmcnt4);
     asm volatile("s_barrier" ::: "memory");
     float s_cur[4];
@@ -583,11 +585,11 @@ gemm_ring_kernel(TiledArgs p) {
           __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j & 1], af[i], zero, 0, 0, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if ((t & 3) == 1) {
-        const int q = t >> 2;  // B_{k+1} parts 0..3, then A_{k+2} parts 0..3
+        const int q = t >> 2;  // A_{k+1} parts 0..3, then B_{k+2} parts 0..3
         if (q < 4)
-          ldb.issue_at(bbase, kb1, wb, wave, q);
+          lda.issue_at(p.a, kb1, wa, wave, q);
         else
-          lda.issue_at(p.a, kb2, wa, wave, q - 4);
+          ldb.issue_at(bbase, kb2, wb, wave, q - 4);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i == 0 && j < 7) {
@@ -603,20 +605,21 @@ gemm_ring_kernel(TiledArgs p) {
     acc[3][7] += part[1] * s_cur[3];
   };
 
-  // A_k sits in slot 2k mod 5 and B_k in 2k+1 mod 5: the pattern repeats
-  // every five steps
+  // A_k sits in slot 2k+1 mod 5 and B_k in 2k mod 5; step k fills the two
+  // slots step k-1 read with A_{k+1} and B_{k+2}.  The pattern repeats every
+  // five steps
   int kb = 0;
   for (; kb + 5 <= p.nkb; kb += 5) {
-    step(r0, r1, r3, r4, kb);
-    step(r2, r3, r0, r1, kb + 1);
-    step(r4, r0, r2, r3, kb + 2);
-    step(r1, r2, r4, r0, kb + 3);
-    step(r3, r4, r1, r2, kb + 4);
+    step(r1, r0, r3, r4, kb);
+    step(r3, r2, r0, r1, kb + 1);
+    step(r0, r4, r2, r3, kb + 2);
+    step(r2, r1, r4, r0, kb + 3);
+    step(r4, r3, r1, r2, kb + 4);
   }
-  if (kb < p.nkb) step(r0, r1, r3, r4, kb);
-  if (kb + 1 < p.nkb) step(r2, r3, r0, r1, kb + 1);
-  if (kb + 2 < p.nkb) step(r4, r0, r2, r3, kb + 2);
-  if (kb + 3 < p.nkb) step(r1, r2, r4, r0, kb + 3);
+  if (kb < p.nkb) step(r1, r0, r3, r4, kb);
+  if (kb + 1 < p.nkb) step(r3, r2, r0, r1, kb + 1);
+  if (kb + 2 < p.nkb) step(r0, r4, r2, r3, kb + 2);
+  if (kb + 3 < p.nkb) step(r2, r1, r4, r0, kb + 3);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
