@@ -90,6 +90,9 @@ def _load():
     lib.orc_grouped_gemm_contig.restype = ctypes.c_int
     lib.orc_grouped_gemm_contig.argtypes = [u8p, f32p, ctypes.c_int, u8p, f32p, i32p,
                                             ctypes.c_int, i64, i64, i64, i64, i64, f64p]
+    lib.orc_grouped_gemm_masked.restype = ctypes.c_int
+    lib.orc_grouped_gemm_masked.argtypes = [u8p, f32p, ctypes.c_int, u8p, f32p, i32p,
+                                            ctypes.c_int, i64, i64, i64, f64p]
     _lib = lib
     return lib
 
@@ -259,6 +262,32 @@ def grouped_gemm_contig(qa, sa, qb, sb, m_indices, a_block_rows: int = 128,
                                          G, M, N, K, r0, r1, _ptr(ref, ctypes.c_double))
     if rc != 0:
         raise ValueError("oracle grouped_gemm_contig rejected its input")
+    return ref
+
+
+def grouped_gemm_masked(qa, sa, qb, sb, masked_m, a_block_rows: int = 1) -> np.ndarray:
+    """Masked grouped product (pzsr.cn DeepGEMM page s2.3, s3.2: expert
+    weights batched in one call; the decode-time layout with a fixed capacity
+    of max_m rows per expert, masked_m[g] of them valid).
+    qa [G, max_m, K], sa [G, ceil(K/128), ceil(max_m/br)], qb [G, N, K],
+    sb [G, ceil(K/128), ceil(N/128)], masked_m int32 [G] in [0, max_m].
+    Returns float64 [G, max_m, N]; rows past masked_m[g] are NaN."""
+    qa, qb = _c(qa, np.uint8), _c(qb, np.uint8)
+    sa, sb = _c(sa, np.float32), _c(sb, np.float32)
+    G, max_m, K = qa.shape
+    N = qb.shape[1]
+    assert qb.shape == (G, N, K)
+    assert sa.shape == (G, cdiv(K, 128), cdiv(max_m, a_block_rows))
+    assert sb.shape == (G, cdiv(K, 128), cdiv(N, 128))
+    mm = _c(masked_m, np.int32)
+    assert mm.shape == (G,)
+    ref = np.full((G, max_m, N), np.nan, dtype=np.float64)
+    rc = _load().orc_grouped_gemm_masked(_ptr(qa, ctypes.c_uint8), _ptr(sa, ctypes.c_float),
+                                         a_block_rows, _ptr(qb, ctypes.c_uint8),
+                                         _ptr(sb, ctypes.c_float), _ptr(mm, ctypes.c_int32),
+                                         G, max_m, N, K, _ptr(ref, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("oracle grouped_gemm_masked rejected its input")
     return ref
 
 

@@ -403,6 +403,40 @@ int orc_grouped_gemm_contig(const uint8_t *qa, const float *sa, int a_block_rows
     return 0;
 }
 
+/* Masked grouped GEMM ("DeepGEMM: GPU high-efficiency BLAS kernel library", */
+/* s2.3 and s3.2: expert weights batched in one grouped call; the layout is  */
+/* the decode-time one, where each expert's row count is known only on the   */
+/* device): group g owns a fixed capacity of max_m rows of A and C, of which */
+/* the first masked_m[g] are valid.  ref[g][m] = A[g][m] . B[g]^T with the   */
+/* group's scales for m < masked_m[g]; the other rows of ref are not written */
+/* (the caller pre-fills them).  masked_m[g] must lie in [0, max_m].          */
+int orc_grouped_gemm_masked(const uint8_t *qa, const float *sa, int a_block_rows,
+                            const uint8_t *qb, const float *sb, const int32_t *masked_m,
+                            int num_groups, int64_t max_m, int64_t N, int64_t K, double *ref)
+{
+    int64_t g, m, n, sa_stride, n_nb, n_kb;
+    if (check_gemm_args(qa, sa, a_block_rows, qb, sb, max_m, N, K) || !masked_m || !ref ||
+        num_groups < 1)
+        return -1;
+    sa_stride = ceil_div(max_m, a_block_rows);
+    n_nb = ceil_div(N, 128);
+    n_kb = ceil_div(K, 128);
+    for (g = 0; g < num_groups; ++g) {
+        const uint8_t *ag = qa + g * max_m * K;
+        const float *sag = sa + g * n_kb * sa_stride;
+        const uint8_t *bg = qb + g * N * K;
+        const float *sbg = sb + g * n_kb * n_nb;
+        if (masked_m[g] < 0 || masked_m[g] > max_m)
+            return -1;
+        for (m = 0; m < masked_m[g]; ++m)
+            for (n = 0; n < N; ++n)
+                ref[(g * max_m + m) * N + n] =
+                    dot_entry(ag + m * K, bg + n * K, sag, sa_stride, m / a_block_rows,
+                              sbg, n_nb, n / 128, K);
+    }
+    return 0;
+}
+
 /* K-grouped GEMM ("DeepGEMM: GPU high-efficiency BLAS kernel library",     */
 /* s3.2: grouped GEMM along the K axis, for MoE weight gradients): group g  */
 /* owns the K range [k_offsets[g], k_offsets[g+1]) (multiples of 128) and    */

@@ -22,7 +22,9 @@
  *     s3.1  NT layout (A not transposed, B transposed); SM90 FP32 scales;
  *           SM100 UE8M0 scales, four packed per 32-bit integer
  *     s3.2, s3.3  grouped GEMM along M for MoE, contiguous layout with an
- *           M alignment per group
+ *           M alignment per group; grouping along K (weight gradients)
+ *     s2.3  grouped GEMM batching the experts' weights (the masked,
+ *           fixed-capacity decode layout is a reading of it)
  *     s4.1  to_fp8(a) -> (a_fp8, a_sf); fp8_gemm_nt(c, a, b, a_sf, b_sf)
  *
  * Parity status: every function here is pinned by the CPU tests (exhaustive
@@ -101,6 +103,12 @@ int orc_grouped_gemm_contig(const uint8_t *qa, const float *sa, int a_block_rows
  * [k_offsets[g], k_offsets[g+1]) (multiples of 128, non-decreasing, within
  * K); out [G][M][N] = per-group dequantised A . B^T over that range, FP64.
  * A [M][K], B [N][K] K-major; scales as orc_gemm_nt over the whole K. */
+/* Masked grouped layout: A [G][max_m][K], sa [G][K/128][ceil(max_m/a_block_rows)],
+ * B [G][N][K], sb [G][K/128][ceil(N/128)], masked_m int32 [G] in [0, max_m];
+ * ref [G][max_m][N]: rows m < masked_m[g] written, the others untouched. */
+int orc_grouped_gemm_masked(const uint8_t *qa, const float *sa, int a_block_rows,
+                            const uint8_t *qb, const float *sb, const int32_t *masked_m,
+                            int num_groups, int64_t max_m, int64_t N, int64_t K, double *ref);
 int orc_grouped_gemm_k(const uint8_t *qa, const float *sa, int a_block_rows,
                        const uint8_t *qb, const float *sb, const int64_t *k_offsets,
                        int num_groups, int64_t M, int64_t N, int64_t K, double *out);
