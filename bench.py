@@ -25,7 +25,8 @@ heavy-tailed, hot-channel activations and 1x128 activation scales),
 scaled matrix instruction), --config epilogue (SwiGLU and in-place residual
 fused into the write-back of MLP-shaped GEMMs, against the unfused pair),
 --config wgrad (MoE weight gradient: token-major operands transposed, then
-the K-grouped GEMM), --config copy (a plain device copy of known size, used to calibrate the
+the K-grouped GEMM), --config masked (decode-time MoE on the masked grouped
+layout: 8 experts with a capacity of 32 rows, 64 tokens top-2), --config copy (a plain device copy of known size, used to calibrate the
 FETCH_SIZE/WRITE_SIZE counters), --config peak (the FP8 MFMA-loop probe: the
 matrix-core rate and shader clock this GPU sustains; the dense line also
 carries it as roofline.measured_peak).
@@ -684,6 +685,82 @@ class Moe:
         return None
 
 
+class Masked:
+    """Decode-time MoE on the masked grouped layout: 8 experts, 64 tokens
+    routed top-2 (uniform, distinct experts), a capacity of 32 rows per
+    expert with masked_m = the routed count; up (N 11008, K 4096) and down
+    (N 4096, K 11008) projections.  Activations arrive quantised per expert
+    (1x128 scales); the step is the two masked GEMMs."""
+    rot = 1
+
+    def __init__(self, dg, seed=0):
+        self.dg = dg
+        G, tokens, H, I, cap = 8, 64, 4096, 11008, 32
+        r = datagen.moe_routing(tokens, G, 2, align=1, seed=seed)
+        counts = np.minimum(r["counts"], cap).astype(np.int32)
+        self.counts = counts
+        self.real_rows = int(counts.sum())
+        mm = torch.from_numpy(counts).cuda()
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        self.items = []
+        for (N, K) in ((I, H), (H, I)):
+            qb = torch.randint(0, 0x7E, (G, N, K), dtype=torch.uint8, device="cuda", generator=gen)
+            sb = torch.rand((G, K // 128, N // 128), device="cuda", generator=gen) * 1e-3
+            qa = torch.randint(0, 0x7E, (G, cap, K), dtype=torch.uint8, device="cuda",
+                               generator=gen)
+            sa = torch.rand((G, K // 128, cap), device="cuda", generator=gen) * 1e-2
+            ws_bytes = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, cap, N, K)
+            self.items.append(dict(
+                G=G, cap=cap, N=N, K=K, qb=qb, sb=sb, qa=qa, sa=sa, mm=mm,
+                ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda"),
+                c=torch.zeros((G, cap, N), dtype=torch.bfloat16, device="cuda")))
+        self.flops = sum(2.0 * self.real_rows * it["N"] * it["K"] for it in self.items)
+
+    def gemm(self, it):
+        self.dg.dg_fp8_grouped_gemm_masked(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], 1,
+                                           it["mm"], workspace=it["ws"])
+
+    def step(self, i=0):
+        for it in self.items:
+            self.gemm(it)
+
+    def outputs(self):
+        return [it["c"] for it in self.items]
+
+    def config(self):
+        return {"workload": "masked grouped MoE GEMM (decode), 8 experts x capacity 32, 64 "
+                            "tokens top-2, hidden 4096, intermediate 11008, up and down "
+                            "projections, A pre-quantised 1x128",
+                "masked_m": self.counts.tolist(), "real_rows": self.real_rows}
+
+    def bytes_of(self, it):
+        # weights + the valid rows of A and C + scales
+        return (it["G"] * it["N"] * it["K"] + self.real_rows * (it["K"] + 2 * it["N"])
+                + 4 * it["G"] * (it["K"] // 128) * (it["cap"] + it["N"] // 128))
+
+    def breakdown(self, timer, reps):
+        out = []
+        for n, it in enumerate(self.items):
+            t = timer.time(lambda: self.gemm(it), reps, key=("masked", n), calls=4)
+            b = self.bytes_of(it)
+            out.append({"nk": [it["N"], it["K"]], "gemm_us": t * 1e3,
+                        "hbm_gbs": b / (t * 1e-3) / 1e9,
+                        "hbm_frac": b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        return out
+
+    def roofline(self, timer, reps):
+        it = self.items[0]
+        t = timer.time(lambda: self.gemm(it), reps, key=("masked", 0), calls=4)
+        ach = self.bytes_of(it) / (t * 1e-3) / 1e9
+        return {"kernel": "masked grouped GEMM up-projection", "bound": "hbm", "achieved": ach,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": None, "avg_launch_us": t * 1e3}
+
+    def cpu_baseline(self):
+        return None
+
+
 def dpm_clocks():
     """Current shader and memory clock levels (MHz) from the amdgpu sysfs DPM
     tables of the card torch uses, or None where they are not readable."""
@@ -783,7 +860,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="dense",
                     choices=["dense", "decode", "moe", "small", "outlier", "ue8m0", "epilogue",
-                             "wgrad", "copy", "peak"])
+                             "wgrad", "masked", "copy", "peak"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -823,6 +900,8 @@ def main():
         w = WeightGrad(dg)
     elif args.config == "decode":
         w = Decode(dg)
+    elif args.config == "masked":
+        w = Masked(dg)
     else:
         w = Moe(dg)
     torch.cuda.synchronize()

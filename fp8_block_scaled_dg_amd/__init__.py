@@ -9,6 +9,8 @@ Entry points (same names as the C ABI):
     dg_quantize_fp8_block(q, scales, x, block_rows)
     dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, workspace=None)
     dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows, m_indices)
+    dg_fp8_grouped_gemm_masked(c, a, b, sa, sb, a_block_rows, masked_m, workspace=None)
+    (and the UE8M0, fused-A, epilogue, layout and K-grouped entry points)
 Conveniences mirroring the DeepGEMM page's Python API (pzsr.cn, s4.1):
     to_fp8(x, block_rows=128) -> (q, scales)
     fp8_gemm_nt(c, a, b, sa, sb, a_block_rows=128)
@@ -73,6 +75,11 @@ def _load():
                                            vp]
     lib.dg_fp8_grouped_gemm_contig.restype = i32
     lib.dg_fp8_grouped_gemm_contig.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
+    lib.dg_fp8_grouped_gemm_masked_workspace_bytes.restype = ctypes.c_size_t
+    lib.dg_fp8_grouped_gemm_masked_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.dg_fp8_grouped_gemm_masked.restype = i32
+    lib.dg_fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp,
+                                               ctypes.c_size_t, vp]
     if lib.dg_abi_version() != ABI_VERSION:
         raise ImportError("libdg ABI %d != binding ABI %d" % (lib.dg_abi_version(), ABI_VERSION))
     return lib
@@ -371,6 +378,36 @@ def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices,
                                           _stream(stream)), "dg_fp8_grouped_gemm_contig")
 
 
+def dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups: int, max_m: int, N: int,
+                                              K: int) -> int:
+    return lib.dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups, max_m, N, K)
+
+
+def dg_fp8_grouped_gemm_masked(c, a, b, sa, sb, a_block_rows: int, masked_m, workspace=None,
+                               stream=None) -> None:
+    """Masked grouped: a [G,max_m,K], b [G,N,K], sa [G,K/128,ceil(max_m/br)],
+    sb [G,K/128,ceil(N/128)], masked_m int32 [G] (device), c [G,max_m,N];
+    rows past masked_m[g] of c[g] are not written."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sa, torch.float32, "sa")
+    _require(sb, torch.float32, "sb")
+    _require(masked_m, torch.int32, "masked_m")
+    G, max_m, K = a.shape
+    Gb, N, Kb = b.shape
+    if Gb != G or Kb != K or c.shape != (G, max_m, N) or masked_m.shape != (G,):
+        raise ValueError("inconsistent masked grouped GEMM shapes")
+    if sa.numel() != G * cdiv(K, 128) * cdiv(max_m, a_block_rows):
+        raise ValueError("sa must hold G*(K/128)*ceil(max_m/a_block_rows) floats")
+    if sb.numel() != G * cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold G*(K/128)*ceil(N/128) floats")
+    _check(lib.dg_fp8_grouped_gemm_masked(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
+                                          a_block_rows, _ptr(masked_m), G, max_m, N, K,
+                                          _ptr(workspace), _workspace_bytes(workspace),
+                                          _stream(stream)), "dg_fp8_grouped_gemm_masked")
+
+
 # ---------------------------------------------------------------------------
 # Conveniences (allocate outputs with torch)
 # ---------------------------------------------------------------------------
@@ -414,4 +451,5 @@ __all__ = [
     "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "to_fp8_ue8m0",
     "dg_fp8_gemm_nt_epilogue", "EPILOGUES", "dg_transpose_fp8", "dg_fp8_gemm_workspace_bytes",
     "dg_fp8_gemm", "LAYOUTS", "dg_fp8_grouped_gemm_k", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
+    "dg_fp8_grouped_gemm_masked", "dg_fp8_grouped_gemm_masked_workspace_bytes",
 ]

@@ -266,4 +266,35 @@ int dg_fp8_grouped_gemm_contig(uint16_t* c, const uint8_t* a, const uint8_t* b, 
   return from_hip(dg::launch_gemm_tiled(p, true, static_cast<hipStream_t>(stream)));
 }
 
+size_t dg_fp8_grouped_gemm_masked_workspace_bytes(int num_groups, int64_t max_m, int64_t N,
+                                                  int64_t K) {
+  if (num_groups < 1 || max_m < 1 || N < 1 || K < 1) return 0;
+  return dg::skinny_masked_workspace_bytes(num_groups, max_m, N, K);
+}
+
+int dg_fp8_grouped_gemm_masked(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
+                               const float* sb, int a_block_rows, const int32_t* masked_m,
+                               int num_groups, int64_t max_m, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gemm(c, a, b, sa, sb, a_block_rows, max_m, N, K);
+  if (st != DG_OK) return st;
+  if (!masked_m) return DG_ERR_NULL;
+  if (!aligned(masked_m, 4)) return DG_ERR_ALIGN;
+  if (num_groups < 1) return DG_ERR_UNSUPPORTED;
+  if (max_m > INT64_MAX / K / num_groups || max_m > INT64_MAX / N / num_groups)
+    return DG_ERR_SHAPE;
+  if (dg::skinny_masked_grid(num_groups, max_m, N, K) > INT32_MAX) return DG_ERR_SHAPE;
+  if (workspace != nullptr && workspace_bytes > 0) {
+    if (workspace_bytes < dg::skinny_masked_workspace_bytes(num_groups, max_m, N, K))
+      return DG_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DG_ERR_ALIGN;
+  } else {
+    workspace = nullptr;
+    workspace_bytes = 0;
+  }
+  dg::GemmProblem p{c, a, b, sa, sb, nullptr, num_groups, a_block_rows, max_m, N, K};
+  return from_hip(dg::launch_gemm_skinny_masked(p, masked_m, max_m, workspace, workspace_bytes,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -71,6 +71,16 @@ hipError_t launch_gemm_skinny(const GemmProblem& p, void* workspace, size_t work
 hipError_t launch_gemm_skinny_fused_a(const GemmProblem& p, const float* af, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
+// Masked grouped layout on the small-M ring kernel: A [G][max_m][K], C
+// [G][max_m][N], masked_m[g] valid rows per group (device int32, clamped into
+// [0, max_m]); p.M is unused, p.num_groups = G.  Workspace as for the plain
+// call (null: no split-K); the grid size is checked against launch limits by
+// the caller.
+size_t skinny_masked_workspace_bytes(int num_groups, int64_t max_m, int64_t N, int64_t K);
+int64_t skinny_masked_grid(int num_groups, int64_t max_m, int64_t N, int64_t K);
+hipError_t launch_gemm_skinny_masked(const GemmProblem& p, const int32_t* masked_m, int64_t max_m,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 // Streaming small-M kernel (no workspace), and whether it is the better of
 // the two small-M kernels for a shape.
 hipError_t launch_gemm_stream(const GemmProblem& p, hipStream_t stream);

@@ -55,13 +55,18 @@ struct SkinnyArgs {
   const uint8_t* b;
   const float* sa;
   const float* sb;
-  float* partials;  // [S][M][N] when S > 1
+  float* partials;  // split s at partials + s * part_stride, row-major [.][N], when S > 1
+  int64_t part_stride;
   int a_block_rows;
   int M, N, K;
   int nkb;
-  int sa_stride;  // ceil(M / a_block_rows)
+  int sa_stride;  // ceil(M / a_block_rows)  (masked: ceil(max_m / a_block_rows))
   int sb_stride;  // ceil(N / 128)
   int S;          // K splits
+  // masked grouped layout: group g has max_m rows of A and C, masked_m[g] of
+  // them valid; the grid covers groups x chunks (MP rows each) x N tiles
+  const int32_t* masked_m;
+  int max_m, chunks, tiles;
 };
 
 __device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 1); }
@@ -92,10 +97,16 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
 // Measured on MI355X over the nine decode shapes: 4 or 6 slots (one
 // workgroup per CU) are no faster than 3 at the best split count, so the
 // launches use 3.
-template <int MP, int F, bool AF32 = false, bool E8 = false, int NS = 3>
-__global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
+// MASKED: the masked grouped layout (a reading of the grouped GEMM of the
+// pzsr.cn DeepGEMM page, s2.3 and s3.2, for decode-time MoE): workgroup
+// (g, chunk, N tile, split) computes rows [chunk * MP, chunk * MP + MP) of
+// group g that are below masked_m[g] (clamped into [0, max_m]), with A, the
+// scales, B and C offset to that group; a chunk with no valid row exits.
+template <int MP, int F, bool AF32 = false, bool E8 = false, int NS = 3, bool MASKED = false>
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   static_assert(!AF32 || MP == 16, "in-kernel quantisation covers up to 16 rows");
   static_assert(!(AF32 && E8), "in-kernel quantisation uses FP32 scales");
+  static_assert(!(MASKED && (AF32 || E8)), "masked layout: E4M3 A with FP32 scales");
   constexpr int BNT = 64 * F;                     // B rows per workgroup (F fragments per wave)
   constexpr int MPE = MP < 32 ? 32 : MP;          // A rows staged (>= 4 DMA instructions)
   constexpr int B_BYTES = BNT * BK;               // 8 or 16 KB
@@ -125,8 +136,28 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nt = blockIdx.x / p.S;
-  const int split = blockIdx.x - nt * p.S;
+  const int tile = blockIdx.x / args.S;  // also the split-K counter index
+  const int split = blockIdx.x - tile * args.S;
+  SkinnyArgs p = args;
+  int nt = tile;
+  if constexpr (MASKED) {
+    const int gc = tile / p.tiles;
+    nt = tile - gc * p.tiles;
+    const int g = gc / p.chunks;
+    const int r0 = (gc - g * p.chunks) * MP;
+    int valid = p.masked_m[g];
+    valid = valid < 0 ? 0 : (valid > p.max_m ? p.max_m : valid);
+    const int rows = valid - r0 < MP ? valid - r0 : MP;
+    if (rows <= 0) return;  // uniform: before any barrier
+    const int64_t row0 = (int64_t)g * p.max_m + r0;
+    p.a += row0 * p.K;
+    p.sa += (int64_t)g * p.nkb * p.sa_stride + (p.a_block_rows == 1 ? r0 : r0 / 128);
+    p.b += (int64_t)g * p.N * p.K;
+    p.sb += (int64_t)g * p.nkb * p.sb_stride;
+    p.c += row0 * p.N;
+    if (p.S > 1) p.partials += row0 * p.N;
+    p.M = rows;
+  }
   const int n0 = nt * BNT;
   const int kb0 = (int)((int64_t)split * p.nkb / p.S);
   const int kb1 = (int)((int64_t)(split + 1) * p.nkb / p.S);
@@ -349,7 +380,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   // with device-scope (relaxed atomic) stores, which are written through to
   // the device-coherent level, and read back with device-scope loads; a full
   // __threadfence() would instead write back each XCD's whole L2.
-  float* mine = p.partials + (int64_t)split * p.M * p.N;
+  float* mine = p.partials + (int64_t)split * p.part_stride;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int m = 16 * i + fr;
@@ -372,7 +403,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
   __syncthreads();  // ... and so have those of every wave of the workgroup
   if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(&g_splitk_counters[nt], 1, __ATOMIC_RELAXED,
+    const int prev = __hip_atomic_fetch_add(&g_splitk_counters[tile], 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == p.S - 1);
   }
@@ -409,7 +440,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
         const int sp = s0 + g;
         if (sp < p.S && live[j]) {
           const uint64_t* src =
-              reinterpret_cast<const uint64_t*>(p.partials + (int64_t)sp * p.M * p.N + off[j]);
+              reinterpret_cast<const uint64_t*>(p.partials + (int64_t)sp * p.part_stride + off[j]);
           part[g][j][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           part[g][j][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -440,7 +471,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs p) {
     }
   });
   if (threadIdx.x == 0)  // leave the counter zeroed for the next call
-    __hip_atomic_store(&g_splitk_counters[nt], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&g_splitk_counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Optional override for tuning sweeps: DG_SKINNY_SPLITS=<S> (read once).
@@ -523,6 +554,9 @@ hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, voi
   if (workspace == nullptr || workspace_bytes < skinny_workspace_bytes(q.M, q.N, q.K)) S = 1;
   p.S = S;
   p.partials = static_cast<float*>(workspace);
+  p.part_stride = q.M * q.N;
+  p.masked_m = nullptr;
+  p.max_m = p.chunks = p.tiles = 0;
   const unsigned grid = (unsigned)(((q.N + 127) / 128) * S);
   hipLaunchKernelGGL((gemm_skinny_kernel<16, 2, true>), dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
@@ -563,10 +597,91 @@ hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t work
   if (workspace == nullptr || workspace_bytes < skinny_workspace_bytes(q.M, q.N, q.K)) S = 1;
   p.S = S;
   p.partials = static_cast<float*>(workspace);
+  p.part_stride = q.M * q.N;
+  p.masked_m = nullptr;
+  p.max_m = p.chunks = p.tiles = 0;
   const int bn = choose_bn(q.M, q.N);
   const unsigned grid = (unsigned)(((q.N + bn - 1) / bn) * S);
   return q.sfa ? launch_mp<true>(p, bn, q.M, grid, stream)
                : launch_mp<false>(p, bn, q.M, grid, stream);
+}
+
+
+namespace {
+
+struct MaskedPlan {
+  int mp, bn, chunks, tiles, S;
+};
+
+// Rows per chunk (the kernel's MP: 16, 32 or 64), B tile rows and splits for
+// the masked layout, planned like a dense small-M call whose N spans every
+// group and chunk.
+MaskedPlan plan_masked(int num_groups, int64_t max_m, int64_t N, int64_t K) {
+  MaskedPlan m;
+  m.mp = max_m <= 16 ? 16 : (max_m <= 32 ? 32 : 64);
+  m.chunks = (int)((max_m + m.mp - 1) / m.mp);
+  const int64_t mc = max_m < m.mp ? max_m : m.mp;
+  const int64_t span = N * num_groups * m.chunks;
+  m.bn = choose_bn(mc, span);
+  m.tiles = (int)((N + m.bn - 1) / m.bn);
+  m.S = choose_splits(mc, span, K);
+  if ((int64_t)num_groups * m.chunks * m.tiles > kMaxCounters) m.S = 1;
+  return m;
+}
+
+template <int MP>
+void launch_masked_mp(const SkinnyArgs& p, int bn, unsigned grid, hipStream_t stream) {
+  if (bn == 64)
+    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 1, false, false, 3, true>), dim3(grid), dim3(256),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 2, false, false, 3, true>), dim3(grid), dim3(256),
+                       0, stream, p);
+}
+
+}  // namespace
+
+size_t skinny_masked_workspace_bytes(int num_groups, int64_t max_m, int64_t N, int64_t K) {
+  const MaskedPlan m = plan_masked(num_groups, max_m, N, K);
+  return m.S > 1 ? (size_t)m.S * (size_t)num_groups * (size_t)max_m * (size_t)N * sizeof(float)
+                 : 0;
+}
+
+int64_t skinny_masked_grid(int num_groups, int64_t max_m, int64_t N, int64_t K) {
+  const MaskedPlan m = plan_masked(num_groups, max_m, N, K);
+  return (int64_t)num_groups * m.chunks * m.tiles * m.S;
+}
+
+hipError_t launch_gemm_skinny_masked(const GemmProblem& q, const int32_t* masked_m, int64_t max_m,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const MaskedPlan m = plan_masked(q.num_groups, max_m, q.N, q.K);
+  SkinnyArgs p;
+  p.c = q.c; p.a = q.a; p.af = nullptr; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
+  p.sfa = nullptr; p.sfb = nullptr;
+  p.epi = Epilogue{};
+  p.epi.ldc = q.N;
+  p.a_block_rows = q.a_block_rows;
+  p.M = 0;  // per workgroup: the valid rows of its chunk
+  p.N = (int)q.N; p.K = (int)q.K;
+  p.nkb = (int)(q.K / BK);
+  p.sa_stride = (int)((max_m + q.a_block_rows - 1) / q.a_block_rows);
+  p.sb_stride = (int)((q.N + 127) / 128);
+  int S = m.S;
+  if (workspace == nullptr ||
+      workspace_bytes < skinny_masked_workspace_bytes(q.num_groups, max_m, q.N, q.K))
+    S = 1;
+  p.S = S;
+  p.partials = static_cast<float*>(workspace);
+  p.part_stride = (int64_t)q.num_groups * max_m * q.N;
+  p.masked_m = masked_m;
+  p.max_m = (int)max_m;
+  p.chunks = m.chunks;
+  p.tiles = m.tiles;
+  const unsigned grid = (unsigned)((int64_t)q.num_groups * m.chunks * m.tiles * S);
+  if (m.mp == 16) launch_masked_mp<16>(p, m.bn, grid, stream);
+  else if (m.mp == 32) launch_masked_mp<32>(p, m.bn, grid, stream);
+  else launch_masked_mp<64>(p, m.bn, grid, stream);
+  return hipGetLastError();
 }
 
 }  // namespace dg

@@ -271,6 +271,38 @@ int dg_fp8_grouped_gemm_contig(uint16_t *c, const uint8_t *a, const uint8_t *b,
                                const int32_t *m_indices, int num_groups,
                                int64_t M, int64_t N, int64_t K, void *stream);
 
+/*
+ * Grouped GEMM, masked layout [D s2.3, s3.2: expert weights batched in one
+ * grouped call].  The layout is a reading for decode-time MoE, where each
+ * expert's token count is known only on the device: every expert has a fixed
+ * capacity of max_m rows, and only the first masked_m[g] are computed.
+ *   a        : E4M3 [num_groups][max_m][K].
+ *   sa       : FP32 [num_groups][K/128][ceil(max_m/a_block_rows)], a_block_rows
+ *              in {1, 128}.
+ *   b        : E4M3 [num_groups][N][K]; sb: FP32 [num_groups][K/128][ceil(N/128)].
+ *   masked_m : DEVICE int32 [num_groups], 4-byte aligned: valid rows of each
+ *              group (values below 0 count as 0, above max_m as max_m).
+ *   c        : out, BF16 [num_groups][max_m][N].  Rows m < masked_m[g] of
+ *              group g get C[g][m] = A[g][m] . B[g]^T (scales as in
+ *              dg_fp8_gemm_nt with the group's scale arrays); the other rows
+ *              are not written.
+ *   workspace: optional split-K scratch, as for dg_fp8_gemm_nt; its size is
+ *              dg_fp8_grouped_gemm_masked_workspace_bytes (0: none needed).
+ *              A call that uses it must not overlap another split-K call on
+ *              the same GPU.
+ * Requirements: those of dg_fp8_gemm_nt with M = max_m (max_m >= 1; N >= 8,
+ * N % 8 == 0; K % 128 == 0; max_m*K and N*K below 2^32); 1 <= num_groups.
+ * Rows are processed in chunks of up to 64 per workgroup, so B is streamed
+ * once per chunk: the layout is meant for max_m <= 64.
+ */
+size_t dg_fp8_grouped_gemm_masked_workspace_bytes(int num_groups, int64_t max_m, int64_t N,
+                                                  int64_t K);
+int dg_fp8_grouped_gemm_masked(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                               const float *sa, const float *sb, int a_block_rows,
+                               const int32_t *masked_m, int num_groups, int64_t max_m,
+                               int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

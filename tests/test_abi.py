@@ -30,7 +30,8 @@ def test_header_declares_the_boundary():
                  "dg_get_mk_alignment_for_contiguous_layout", "dg_fp8_gemm_nt_fused_a",
                  "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_fp8_gemm_nt_epilogue",
                  "dg_transpose_fp8", "dg_fp8_gemm", "dg_fp8_gemm_workspace_bytes",
-                 "dg_fp8_grouped_gemm_k"):
+                 "dg_fp8_grouped_gemm_k", "dg_fp8_grouped_gemm_masked",
+                 "dg_fp8_grouped_gemm_masked_workspace_bytes"):
         assert need in names
 
 
@@ -194,3 +195,21 @@ def test_layouts_transpose_and_k_grouped_validation(dg):
     assert gk(G=0) == 3
     assert gk(ko=ctypes.c_void_p(0x10004)) == 4
     assert gk(K=200) == 2
+
+
+def test_masked_grouped_validation(dg):
+    lib = dg.lib
+
+    def gm(c=P, mm=P, G=8, max_m=16, N=512, K=512, br=1, ws=None, wsb=0):
+        return lib.dg_fp8_grouped_gemm_masked(c, P, P, P, P, br, mm, G, max_m, N, K, ws, wsb,
+                                              None)
+    assert gm(c=None) == 1 and gm(mm=None) == 1
+    assert gm(G=0) == 3 and gm(br=64) == 3
+    assert gm(max_m=0) == 2 and gm(N=100) == 2 and gm(K=200) == 2
+    assert gm(mm=ctypes.c_void_p(0x10002)) == 4 and gm(c=P1) == 4
+    need = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(8, 16, 512, 4096)
+    assert need > 16                      # this shape plans a split-K reduction
+    assert need == dg.dg_fp8_grouped_gemm_masked_workspace_bytes(8, 16, 512, 4096)
+    assert gm(K=4096, ws=P, wsb=16) == 5
+    assert gm(K=4096, ws=P1, wsb=need) == 4
+    assert dg.dg_fp8_grouped_gemm_masked_workspace_bytes(0, 16, 512, 4096) == 0
