@@ -128,3 +128,21 @@ def test_graph_k_grouped(dg, orc):
     ko = torch.tensor([0, 384, 384, 1024, 1664], dtype=torch.int64, device="cuda")
     check_graph(lambda: [torch.empty((4, M, N), dtype=torch.bfloat16, device="cuda")],
                 lambda o: dg.dg_fp8_grouped_gemm_k(o[0], qa, qb, sa, sb, 1, ko))
+
+
+def test_graph_masked_grouped(dg, orc):
+    G, max_m, N, K = 8, 16, 1024, 2048
+    qa = np.empty((G, max_m, K), np.uint8)
+    sa = np.empty((G, K // 128, max_m), np.float32)
+    qb = np.empty((G, N, K), np.uint8)
+    sb = np.empty((G, K // 128, N // 128), np.float32)
+    for g in range(G):
+        qa[g], sa[g] = orc.quantize(datagen.normal((max_m, K), 1.0, seed=g, stream=0), 1)
+        qb[g], sb[g] = orc.quantize(datagen.normal((N, K), 0.02, seed=g, stream=1), 128)
+    mm = dev(np.array([16, 0, 5, 16, 9, 1, 12, 3], np.int32))
+    n = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, max_m, N, K)
+    assert n > 0                                  # the split-K plan (counters across replays)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    A, B, SA, SB = dev(qa), dev(qb), dev(sa), dev(sb)
+    check_graph(lambda: [torch.zeros((G, max_m, N), dtype=torch.bfloat16, device="cuda")],
+                lambda o: dg.dg_fp8_grouped_gemm_masked(o[0], A, B, SA, SB, 1, mm, workspace=ws))
