@@ -104,3 +104,35 @@ def test_all_groups_empty_writes_nothing(dg, orc):
     qa, sa, qb, sb = operands(orc, 4, 16, 256, 256, 1, seed=9)
     bits, _ = run(dg, qa, sa, qb, sb, [0, 0, 0, 0], 1, True)
     assert np.all(bits == SENTINEL)
+
+
+@pytest.mark.parametrize("N,K", [(11008, 4096), (4096, 11008)])
+def test_masked_decode_moe_full_size_sampled(dg, orc, N, K):
+    """The bench's decode MoE workload: 8 experts with a capacity of 32
+    rows, 64 tokens routed top-2 (the routed counts are the masks), up and
+    down projections; 2000 sampled valid outputs against the oracle, every
+    row past the counts untouched."""
+    G, cap = 8, 32
+    r = datagen.moe_routing(64, G, 2, align=1, seed=0)
+    mm = np.minimum(r["counts"], cap).astype(np.int32)
+    qa = np.empty((G, cap, K), np.uint8)
+    sa = np.empty((G, K // 128, cap), np.float32)
+    qb = np.empty((G, N, K), np.uint8)
+    sb = np.empty((G, K // 128, N // 128), np.float32)
+    w = datagen.normal((G * N, K), 0.02, seed=0, stream=2)
+    for g in range(G):
+        qa[g], sa[g] = orc.quantize(datagen.normal((cap, K), 1.0, seed=0, stream=10 + g), 1)
+        qb[g], sb[g] = orc.quantize(w[g * N:(g + 1) * N], 128)
+    bits, c = run(dg, qa, sa, qb, sb, mm, 1, True)
+    for g in range(G):
+        assert np.all(bits[g, mm[g]:] == SENTINEL)
+    rng = np.random.default_rng(3)
+    pg = rng.integers(0, G, 2000)
+    pm = (rng.random(2000) * mm[pg]).astype(np.int64)
+    pn = rng.integers(0, N, 2000)
+    ref = np.empty(2000)
+    for g in range(G):
+        sel = pg == g
+        ref[sel] = orc.gemm_nt_points(qa[g], sa[g], qb[g], sb[g], pm[sel], pn[sel], a_block_rows=1)
+    assert_close(c[pg, pm, pn], ref, rms=float(np.sqrt(np.mean(ref ** 2))),
+                 what="masked decode MoE %dx%d" % (N, K))
