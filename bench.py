@@ -643,10 +643,31 @@ class Moe:
                 sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
                 c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         self.flops = sum(2.0 * self.real_rows * it["N"] * it["K"] for it in self.items)
+        # breakdown only: the up projection with gate and up interleaved
+        # (2 x 11008 rows per expert) and SwiGLU fused on the write-back
+        up = self.items[0]
+        self.glu = dict(
+            qb=torch.randint(0, 0x7E, (G, 2 * I, H), dtype=torch.uint8, device="cuda", generator=gen),
+            sb=torch.rand((G, H // 128, 2 * I // 128), device="cuda", generator=gen) * 1e-3,
+            c=torch.empty((M, I), dtype=torch.bfloat16, device="cuda"),
+            c_full=torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda"), up=up)
 
     def gemm(self, it):
         self.dg.dg_fp8_grouped_gemm_contig(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], 1,
                                            it["mi"])
+
+    def glu_fused(self):
+        g, up = self.glu, self.glu["up"]
+        self.dg.dg_fp8_grouped_gemm_contig(g["c"], up["qa"], g["qb"], up["sa"], g["sb"], 1,
+                                           up["mi"], act="swiglu")
+
+    def glu_unfused(self):
+        g, up = self.glu, self.glu["up"]
+        self.dg.dg_fp8_grouped_gemm_contig(g["c_full"], up["qa"], g["qb"], up["sa"], g["sb"], 1,
+                                           up["mi"])
+        gate = g["c_full"][:, 0::2].float()
+        u = g["c_full"][:, 1::2].float()
+        g["c"].copy_(torch.nn.functional.silu(gate) * u)
 
     def step(self, i=0):
         for it in self.items:
@@ -670,6 +691,13 @@ class Moe:
                         "tflops_real_rows": 2.0 * self.real_rows * it["N"] * it["K"]
                         / (t * 1e-3) / 1e12,
                         "hbm_gbs": byts / (t * 1e-3) / 1e9})
+        up = self.items[0]
+        tf = timer.time(self.glu_fused, reps, key=("moeglu", 0), calls=4)
+        tu = timer.time(self.glu_unfused, reps, key=("moeglu", 1), calls=4)
+        out.append({"nk": [2 * up["N"], up["K"]], "epilogue": "swiglu (gate/up interleaved)",
+                    "fused_us": tf * 1e3, "unfused_us": tu * 1e3,
+                    "tflops_real_rows": 2.0 * self.real_rows * 2 * up["N"] * up["K"]
+                    / (tf * 1e-3) / 1e12})
         return out
 
     def roofline(self, timer, reps):

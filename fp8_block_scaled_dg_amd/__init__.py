@@ -77,6 +77,12 @@ def _load():
     lib.dg_fp8_grouped_gemm_contig.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
     lib.dg_fp8_grouped_gemm_masked_workspace_bytes.restype = ctypes.c_size_t
     lib.dg_fp8_grouped_gemm_masked_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    lib.dg_fp8_grouped_gemm_contig_epilogue.restype = i32
+    lib.dg_fp8_grouped_gemm_contig_epilogue.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
+                                                        i64, i32, vp, vp]
+    lib.dg_fp8_grouped_gemm_masked_epilogue.restype = i32
+    lib.dg_fp8_grouped_gemm_masked_epilogue.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
+                                                        i64, i32, vp, vp, ctypes.c_size_t, vp]
     lib.dg_fp8_grouped_gemm_masked.restype = i32
     lib.dg_fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp,
                                                ctypes.c_size_t, vp]
@@ -355,10 +361,12 @@ def dg_fp8_grouped_gemm_k(c, a, b, sa, sb, a_block_rows: int, k_offsets, stream=
            "dg_fp8_grouped_gemm_k")
 
 
-def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices,
-                               stream=None) -> None:
+def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices, act: str = "none",
+                               residual=None, stream=None) -> None:
     """Grouped M-contiguous: a [M,K], b [G,N,K], sb [G,K/128,ceil(N/128)],
-    m_indices int32 [M] (-1 = padding row)."""
+    m_indices int32 [M] (-1 = padding row -> zero row).  act / residual: the
+    fused epilogue (swiglu: each expert's B rows interleave gate and up, c has
+    N/2 columns); padding rows stay zero."""
     c = _bf16(c, "c")
     a = _codes(a, "a")
     b = _codes(b, "b")
@@ -367,15 +375,28 @@ def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices,
     _require(m_indices, torch.int32, "m_indices")
     M, K = a.shape
     G, N, Kb = b.shape
-    if Kb != K or c.shape != (M, N) or m_indices.shape != (M,):
-        raise ValueError("shape mismatch")
+    code = EPILOGUES[act]
+    n_out = N // 2 if code == EPILOGUES["swiglu"] else N
+    if Kb != K or c.shape != (M, n_out) or m_indices.shape != (M,):
+        raise ValueError("inconsistent grouped GEMM shapes")
     if sa.numel() != cdiv(K, 128) * cdiv(M, a_block_rows):
         raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
     if sb.numel() != G * cdiv(K, 128) * cdiv(N, 128):
         raise ValueError("sb must hold G*(K/128)*ceil(N/128) floats")
-    _check(lib.dg_fp8_grouped_gemm_contig(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
-                                          a_block_rows, _ptr(m_indices), G, M, N, K,
-                                          _stream(stream)), "dg_fp8_grouped_gemm_contig")
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        if residual.shape != (M, n_out):
+            raise ValueError("residual must be [M, Nout]")
+    if code == 0 and residual is None:
+        rc = lib.dg_fp8_grouped_gemm_contig(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
+                                            a_block_rows, _ptr(m_indices), G, M, N, K,
+                                            _stream(stream))
+    else:
+        rc = lib.dg_fp8_grouped_gemm_contig_epilogue(_ptr(c), _ptr(a), _ptr(b), _ptr(sa),
+                                                     _ptr(sb), a_block_rows, _ptr(m_indices), G,
+                                                     M, N, K, code, _ptr(residual),
+                                                     _stream(stream))
+    _check(rc, "dg_fp8_grouped_gemm_contig")
 
 
 def dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups: int, max_m: int, N: int,
@@ -384,10 +405,11 @@ def dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups: int, max_m: int, N: i
 
 
 def dg_fp8_grouped_gemm_masked(c, a, b, sa, sb, a_block_rows: int, masked_m, workspace=None,
-                               stream=None) -> None:
+                               act: str = "none", residual=None, stream=None) -> None:
     """Masked grouped: a [G,max_m,K], b [G,N,K], sa [G,K/128,ceil(max_m/br)],
-    sb [G,K/128,ceil(N/128)], masked_m int32 [G] (device), c [G,max_m,N];
-    rows past masked_m[g] of c[g] are not written."""
+    sb [G,K/128,ceil(N/128)], masked_m int32 [G] (device), c [G,max_m,Nout]
+    (Nout = N, or N/2 with act="swiglu"); rows past masked_m[g] of c[g] are
+    not written.  act / residual [G,max_m,Nout]: the fused epilogue."""
     c = _bf16(c, "c")
     a = _codes(a, "a")
     b = _codes(b, "b")
@@ -396,16 +418,30 @@ def dg_fp8_grouped_gemm_masked(c, a, b, sa, sb, a_block_rows: int, masked_m, wor
     _require(masked_m, torch.int32, "masked_m")
     G, max_m, K = a.shape
     Gb, N, Kb = b.shape
-    if Gb != G or Kb != K or c.shape != (G, max_m, N) or masked_m.shape != (G,):
+    code = EPILOGUES[act]
+    n_out = N // 2 if code == EPILOGUES["swiglu"] else N
+    if Gb != G or Kb != K or c.shape != (G, max_m, n_out) or masked_m.shape != (G,):
         raise ValueError("inconsistent masked grouped GEMM shapes")
     if sa.numel() != G * cdiv(K, 128) * cdiv(max_m, a_block_rows):
         raise ValueError("sa must hold G*(K/128)*ceil(max_m/a_block_rows) floats")
     if sb.numel() != G * cdiv(K, 128) * cdiv(N, 128):
         raise ValueError("sb must hold G*(K/128)*ceil(N/128) floats")
-    _check(lib.dg_fp8_grouped_gemm_masked(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
-                                          a_block_rows, _ptr(masked_m), G, max_m, N, K,
-                                          _ptr(workspace), _workspace_bytes(workspace),
-                                          _stream(stream)), "dg_fp8_grouped_gemm_masked")
+    if residual is not None:
+        residual = _bf16(residual, "residual")
+        if residual.shape != (G, max_m, n_out):
+            raise ValueError("residual must be [G, max_m, Nout]")
+    if code == 0 and residual is None:
+        rc = lib.dg_fp8_grouped_gemm_masked(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
+                                            a_block_rows, _ptr(masked_m), G, max_m, N, K,
+                                            _ptr(workspace), _workspace_bytes(workspace),
+                                            _stream(stream))
+    else:
+        rc = lib.dg_fp8_grouped_gemm_masked_epilogue(_ptr(c), _ptr(a), _ptr(b), _ptr(sa),
+                                                     _ptr(sb), a_block_rows, _ptr(masked_m), G,
+                                                     max_m, N, K, code, _ptr(residual),
+                                                     _ptr(workspace), _workspace_bytes(workspace),
+                                                     _stream(stream))
+    _check(rc, "dg_fp8_grouped_gemm_masked")
 
 
 # ---------------------------------------------------------------------------
@@ -453,3 +489,5 @@ __all__ = [
     "dg_fp8_gemm", "LAYOUTS", "dg_fp8_grouped_gemm_k", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
     "dg_fp8_grouped_gemm_masked", "dg_fp8_grouped_gemm_masked_workspace_bytes",
 ]
+# (the _epilogue C entry points are reached through the act / residual
+# arguments of dg_fp8_grouped_gemm_contig and dg_fp8_grouped_gemm_masked)

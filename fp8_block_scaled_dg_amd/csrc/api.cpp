@@ -255,14 +255,27 @@ int dg_fp8_grouped_gemm_k(uint16_t* c, const uint8_t* a, const uint8_t* b, const
 int dg_fp8_grouped_gemm_contig(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
                                const float* sb, int a_block_rows, const int32_t* m_indices,
                                int num_groups, int64_t M, int64_t N, int64_t K, void* stream) {
+  return dg_fp8_grouped_gemm_contig_epilogue(c, a, b, sa, sb, a_block_rows, m_indices, num_groups,
+                                             M, N, K, DG_EPI_NONE, nullptr, stream);
+}
+
+int dg_fp8_grouped_gemm_contig_epilogue(uint16_t* c, const uint8_t* a, const uint8_t* b,
+                                        const float* sa, const float* sb, int a_block_rows,
+                                        const int32_t* m_indices, int num_groups, int64_t M,
+                                        int64_t N, int64_t K, int act, const uint16_t* residual,
+                                        void* stream) {
   int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
   if (st != DG_OK) return st;
   if (!m_indices) return DG_ERR_NULL;
   if (!aligned(m_indices, 4)) return DG_ERR_ALIGN;
   if (num_groups < 1) return DG_ERR_UNSUPPORTED;
+  if (act < DG_EPI_NONE || act > DG_EPI_SWIGLU) return DG_ERR_UNSUPPORTED;
+  if (residual && !aligned(residual, 16)) return DG_ERR_ALIGN;
   if (M % 128 != 0) return DG_ERR_SHAPE;
   if ((int64_t)num_groups * N * K / num_groups != N * K) return DG_ERR_SHAPE;
   dg::GemmProblem p{c, a, b, sa, sb, m_indices, num_groups, a_block_rows, M, N, K};
+  p.epi.act = act;
+  p.epi.res = residual;
   return from_hip(dg::launch_gemm_tiled(p, true, static_cast<hipStream_t>(stream)));
 }
 
@@ -276,11 +289,23 @@ int dg_fp8_grouped_gemm_masked(uint16_t* c, const uint8_t* a, const uint8_t* b, 
                                const float* sb, int a_block_rows, const int32_t* masked_m,
                                int num_groups, int64_t max_m, int64_t N, int64_t K,
                                void* workspace, size_t workspace_bytes, void* stream) {
+  return dg_fp8_grouped_gemm_masked_epilogue(c, a, b, sa, sb, a_block_rows, masked_m, num_groups,
+                                             max_m, N, K, DG_EPI_NONE, nullptr, workspace,
+                                             workspace_bytes, stream);
+}
+
+int dg_fp8_grouped_gemm_masked_epilogue(uint16_t* c, const uint8_t* a, const uint8_t* b,
+                                        const float* sa, const float* sb, int a_block_rows,
+                                        const int32_t* masked_m, int num_groups, int64_t max_m,
+                                        int64_t N, int64_t K, int act, const uint16_t* residual,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_gemm(c, a, b, sa, sb, a_block_rows, max_m, N, K);
   if (st != DG_OK) return st;
   if (!masked_m) return DG_ERR_NULL;
   if (!aligned(masked_m, 4)) return DG_ERR_ALIGN;
   if (num_groups < 1) return DG_ERR_UNSUPPORTED;
+  if (act < DG_EPI_NONE || act > DG_EPI_SWIGLU) return DG_ERR_UNSUPPORTED;
+  if (residual && !aligned(residual, 16)) return DG_ERR_ALIGN;
   if (max_m > INT64_MAX / K / num_groups || max_m > INT64_MAX / N / num_groups)
     return DG_ERR_SHAPE;
   if (dg::skinny_masked_grid(num_groups, max_m, N, K) > INT32_MAX) return DG_ERR_SHAPE;
@@ -293,6 +318,8 @@ int dg_fp8_grouped_gemm_masked(uint16_t* c, const uint8_t* a, const uint8_t* b, 
     workspace_bytes = 0;
   }
   dg::GemmProblem p{c, a, b, sa, sb, nullptr, num_groups, a_block_rows, max_m, N, K};
+  p.epi.act = act;
+  p.epi.res = residual;
   return from_hip(dg::launch_gemm_skinny_masked(p, masked_m, max_m, workspace, workspace_bytes,
                                                 static_cast<hipStream_t>(stream)));
 }

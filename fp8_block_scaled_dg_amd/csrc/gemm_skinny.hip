@@ -154,7 +154,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
     p.sa += (int64_t)g * p.nkb * p.sa_stride + (p.a_block_rows == 1 ? r0 : r0 / 128);
     p.b += (int64_t)g * p.N * p.K;
     p.sb += (int64_t)g * p.nkb * p.sb_stride;
-    p.c += row0 * p.N;
+    p.c += row0 * p.epi.ldc;  // (N / 2 columns with SwiGLU)
+    if (p.epi.res) p.epi.res += row0 * p.epi.ldc;
     if (p.S > 1) p.partials += row0 * p.N;
     p.M = rows;
   }
@@ -658,8 +659,7 @@ hipError_t launch_gemm_skinny_masked(const GemmProblem& q, const int32_t* masked
   SkinnyArgs p;
   p.c = q.c; p.a = q.a; p.af = nullptr; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
   p.sfa = nullptr; p.sfb = nullptr;
-  p.epi = Epilogue{};
-  p.epi.ldc = q.N;
+  p.epi = resolved_epilogue(q);
   p.a_block_rows = q.a_block_rows;
   p.M = 0;  // per workgroup: the valid rows of its chunk
   p.N = (int)q.N; p.K = (int)q.K;

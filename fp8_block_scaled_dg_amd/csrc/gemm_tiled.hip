@@ -172,11 +172,16 @@ __device__ __forceinline__ bool grouped_tile(const TiledArgs& p, int blk, int n0
   m0 = blk * 128;
   const int g = p.m_indices[m0];
   if (g < 0 || g >= p.num_groups) {
-    for (int idx = threadIdx.x; idx < 128 * (BN / 8); idx += blockDim.x) {
-      const int r = idx / (BN / 8);
-      const int cc = (idx % (BN / 8)) * 8;
-      if (n0 + cc < p.N)
-        *reinterpret_cast<uint4*>(p.c + (int64_t)(m0 + r) * p.N + n0 + cc) = make_uint4(0, 0, 0, 0);
+    // the block's output columns (half of the tile's with SwiGLU), 4 per store
+    const bool glu = p.epi.act == EPI_SWIGLU;
+    const int64_t ldc = p.epi.ldc;
+    const int oc0 = glu ? n0 / 2 : n0;
+    constexpr int Q = BN / 4;  // 4-column groups per row (SwiGLU uses the first half)
+    for (int idx = threadIdx.x; idx < 128 * Q; idx += blockDim.x) {
+      const int r = idx / Q;
+      const int cc = (idx % Q) * 4;
+      if ((!glu || cc < BN / 2) && oc0 + cc < ldc)
+        *reinterpret_cast<uint2*>(p.c + (int64_t)(m0 + r) * ldc + oc0 + cc) = make_uint2(0, 0);
     }
     return false;
   }
@@ -199,6 +204,37 @@ __device__ __forceinline__ bool grouped_tile(const TiledArgs& p, int blk, int n0
   bbase += (int64_t)g * p.N * p.K;
   sbbase += (int64_t)g * p.nkb * p.sb_stride;
   return true;
+}
+
+// Grouped epilogue straight from the MFMA layout (lane: 4 consecutive
+// columns of one row per 16 x 16 sub-tile): the fused epilogue on real rows,
+// zeros on padding rows (id -1; with SwiGLU the row's half-width output).
+__device__ __forceinline__ void grouped_store(const TiledArgs& p, const v4f (&acc)[4][8], int m0,
+                                              int nw0, int mw0, int rows_end, int lane) {
+  const int fr = lane & 15;
+  with_epilogue(p.epi, [&](auto act, auto res) {
+    constexpr int ACT = decltype(act)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + mw0 + 16 * i + fr;
+      if (m >= rows_end) continue;
+      const bool zero_row = p.m_indices[m] < 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int n = nw0 + 16 * j + 4 * (lane >> 4);
+        if (n >= p.N) continue;
+        if (zero_row) {
+          if (ACT == EPI_SWIGLU)
+            *reinterpret_cast<uint32_t*>(p.c + (int64_t)m * p.epi.ldc + (n >> 1)) = 0u;
+          else
+            *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.epi.ldc + n) = make_uint2(0, 0);
+        } else {
+          const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+          store4<ACT, decltype(res)::value != 0>(p.c, m, n, t, p.epi);
+        }
+      }
+    }
+  });
 }
 
 // E8: power-of-two (UE8M0) scales (DeepGEMM page on pzsr.cn, s3.1), four K
@@ -386,25 +422,7 @@ gemm_tiled_kernel(TiledArgs p) {
   }
 
   if constexpr (GROUPED) {
-    // epilogue: BF16 round-to-nearest-even, 4 consecutive columns per lane
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 64 + 16 * i + fr;
-      if (m >= rows_end) continue;
-      const bool zero_row = p.m_indices[m] < 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
-        if (n < p.N) {
-          if (zero_row) {
-            *reinterpret_cast<uint2*>(cbase + (int64_t)m * p.N + n) = make_uint2(0, 0);
-          } else {
-            const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            store4<EPI_NONE, false>(cbase, m, n, t, p.epi);  // grouped: no epilogue
-          }
-        }
-      }
-    }
+    grouped_store(p, acc, m0, n0 + wn * 128, wm * 64, rows_end, lane);
   } else {
     // The finished tile leaves through LDS.  Stored straight from the MFMA
     // layout, each store instruction writes 32 bytes into each of 16 rows;
@@ -622,21 +640,19 @@ gemm_ring_kernel(TiledArgs p) {
   if (kb + 3 < p.nkb) step(r2, r1, r4, r0, kb + 3);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+  if constexpr (GROUPED) {
+    grouped_store(p, acc, m0, n0 + wn * 128, wm * 64, rows_end, lane);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 64 + 16 * i + fr;
-    if (m >= rows_end) continue;
-    bool zero_row = false;
-    if (GROUPED) zero_row = p.m_indices[m] < 0;
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + wm * 64 + 16 * i + fr;
+      if (m >= rows_end) continue;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
-      if (n < p.N) {
-        if (zero_row) {
-          *reinterpret_cast<uint2*>(p.c + (int64_t)m * p.N + n) = make_uint2(0, 0);
-        } else {
+      for (int j = 0; j < 8; ++j) {
+        const int n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
+        if (n < p.N) {
           const float t[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-          store4<EPI_NONE, false>(p.c, m, n, t, p.epi);
+          store4<EPI_NONE, false>(p.c, m, n, t, p.epi);  // dense ring: no epilogue
         }
       }
     }

@@ -272,6 +272,21 @@ int dg_fp8_grouped_gemm_contig(uint16_t *c, const uint8_t *a, const uint8_t *b,
                                int64_t M, int64_t N, int64_t K, void *stream);
 
 /*
+ * dg_fp8_grouped_gemm_contig with the fused epilogue of dg_fp8_gemm_nt_epilogue
+ * [M s3.2; D s2.3: SwiGLU inside the MoE kernel] applied to every real row:
+ * act in DG_EPI_*, SwiGLU over interleaved gate/up rows of each expert's B
+ * (C then has N/2 columns), optional BF16 residual [M][Nout] (16-byte
+ * aligned, may be c).  Padding rows are written as zeros (no residual).
+ * An unknown act gives DG_ERR_UNSUPPORTED; the rest as
+ * dg_fp8_grouped_gemm_contig, which is this call with DG_EPI_NONE.
+ */
+int dg_fp8_grouped_gemm_contig_epilogue(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                                        const float *sa, const float *sb, int a_block_rows,
+                                        const int32_t *m_indices, int num_groups, int64_t M,
+                                        int64_t N, int64_t K, int act, const uint16_t *residual,
+                                        void *stream);
+
+/*
  * Grouped GEMM, masked layout [D s2.3, s3.2: expert weights batched in one
  * grouped call].  The layout is a reading for decode-time MoE, where each
  * expert's token count is known only on the device: every expert has a fixed
@@ -302,6 +317,20 @@ int dg_fp8_grouped_gemm_masked(uint16_t *c, const uint8_t *a, const uint8_t *b,
                                const int32_t *masked_m, int num_groups, int64_t max_m,
                                int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * dg_fp8_grouped_gemm_masked with the fused epilogue of
+ * dg_fp8_gemm_nt_epilogue on the valid rows: act in DG_EPI_*, SwiGLU over
+ * interleaved gate/up rows of each expert's B (C then [num_groups][max_m][N/2]),
+ * optional BF16 residual laid out like C (16-byte aligned, may be c).  Rows
+ * past masked_m[g] are not written.  dg_fp8_grouped_gemm_masked is this call
+ * with DG_EPI_NONE and no residual.
+ */
+int dg_fp8_grouped_gemm_masked_epilogue(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                                        const float *sa, const float *sb, int a_block_rows,
+                                        const int32_t *masked_m, int num_groups, int64_t max_m,
+                                        int64_t N, int64_t K, int act, const uint16_t *residual,
+                                        void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

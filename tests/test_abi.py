@@ -213,3 +213,20 @@ def test_masked_grouped_validation(dg):
     assert gm(K=4096, ws=P, wsb=16) == 5
     assert gm(K=4096, ws=P1, wsb=need) == 4
     assert dg.dg_fp8_grouped_gemm_masked_workspace_bytes(0, 16, 512, 4096) == 0
+
+
+def test_grouped_epilogue_validation(dg):
+    lib = dg.lib
+    MI = ctypes.c_void_p(0x10000)
+
+    def ge(act=0, res=None, M=256):
+        return lib.dg_fp8_grouped_gemm_contig_epilogue(P, P, P, P, P, 1, MI, 4, M, 512, 512, act,
+                                                       res, None)
+    assert ge(act=5) == 3 and ge(act=-1) == 3
+    assert ge(res=P1) == 4
+    assert ge(M=200) == 2
+
+    def me(act=0, res=None):
+        return lib.dg_fp8_grouped_gemm_masked_epilogue(P, P, P, P, P, 1, MI, 8, 16, 512, 512, act,
+                                                       res, None, 0, None)
+    assert me(act=7) == 3 and me(res=P1) == 4
