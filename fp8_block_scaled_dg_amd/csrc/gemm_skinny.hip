@@ -614,9 +614,13 @@ struct MaskedPlan {
   int mp, bn, chunks, tiles, S;
 };
 
-// Rows per chunk (the kernel's MP: 16, 32 or 64), B tile rows and splits for
-// the masked layout, planned like a dense small-M call whose N spans every
-// group and chunk.
+// Rows per chunk (the kernel's MP: 16, 32 or 64), B tile rows (as for a
+// dense small-M call whose N spans every group and chunk) and splits for the
+// masked layout.  Splits: a power of two, at most what gives ~768
+// workgroups (two or more per CU hide the weight stream's latency better),
+// at most 8, and at least 16 K blocks each.  Measured on MI355X, 8 experts x capacity 32: up projection
+// (N 11008, K 4096) 88.6 us with 1 split, 81.3 with 2; down (N 4096,
+// K 11008) 85.1 us with 1, 77.0 with 2, 79.5 with 4.
 MaskedPlan plan_masked(int num_groups, int64_t max_m, int64_t N, int64_t K) {
   MaskedPlan m;
   m.mp = max_m <= 16 ? 16 : (max_m <= 32 ? 32 : 64);
@@ -625,8 +629,17 @@ MaskedPlan plan_masked(int num_groups, int64_t max_m, int64_t N, int64_t K) {
   const int64_t span = N * num_groups * m.chunks;
   m.bn = choose_bn(mc, span);
   m.tiles = (int)((N + m.bn - 1) / m.bn);
-  m.S = choose_splits(mc, span, K);
-  if ((int64_t)num_groups * m.chunks * m.tiles > kMaxCounters) m.S = 1;
+  const int64_t wgs = (int64_t)num_groups * m.chunks * m.tiles;
+  int64_t S = forced_splits();
+  if (S <= 0) {
+    const int64_t want = (768 + wgs - 1) / wgs;
+    for (S = 1; 2 * S <= want && 2 * S <= (K / BK) / 16; S *= 2) {
+    }
+  }
+  S = S > 8 ? 8 : S;
+  S = S > K / BK ? K / BK : S;
+  m.S = S < 1 ? 1 : (int)S;
+  if (wgs > kMaxCounters) m.S = 1;
   return m;
 }
 

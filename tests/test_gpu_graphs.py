@@ -131,7 +131,7 @@ def test_graph_k_grouped(dg, orc):
 
 
 def test_graph_masked_grouped(dg, orc):
-    G, max_m, N, K = 8, 16, 1024, 2048
+    G, max_m, N, K = 8, 16, 1024, 4096
     qa = np.empty((G, max_m, K), np.uint8)
     sa = np.empty((G, K // 128, max_m), np.float32)
     qb = np.empty((G, N, K), np.uint8)

@@ -134,7 +134,7 @@ def masked_operands(orc, G, max_m, N, K, seed):
 @pytest.mark.parametrize("act,residual", [("swiglu", True), ("gelu", False), ("relu", True),
                                           ("silu", False)])
 def test_masked_epilogue(dg, orc, act, residual, ws):
-    G, max_m, N, K = 6, 24, 1024, 2048
+    G, max_m, N, K = 6, 24, 1024, 4096
     mm = np.array([24, 0, 7, 13, 1, 24], np.int32)
     qa, sa, qb, sb = masked_operands(orc, G, max_m, N, K, seed=31)
     n_out = N // 2 if act == "swiglu" else N
