@@ -83,6 +83,9 @@ def _load():
     lib.dg_fp8_grouped_gemm_masked_epilogue.restype = i32
     lib.dg_fp8_grouped_gemm_masked_epilogue.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
                                                         i64, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.dg_fp8_grouped_gemm_contig_ue8m0.restype = i32
+    lib.dg_fp8_grouped_gemm_contig_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
+                                                     i64, vp]
     lib.dg_fp8_grouped_gemm_masked.restype = i32
     lib.dg_fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp,
                                                ctypes.c_size_t, vp]
@@ -399,6 +402,29 @@ def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices, ac
     _check(rc, "dg_fp8_grouped_gemm_contig")
 
 
+def dg_fp8_grouped_gemm_contig_ue8m0(c, a, b, sfa, sfb, a_block_rows: int, m_indices,
+                                     stream=None) -> None:
+    """Grouped M-contiguous with packed UE8M0 scales: sfa int32
+    [ceil(K/512), ceil(M/br)], sfb int32 [G, ceil(K/512), ceil(N/128)]."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sfa, torch.int32, "sfa")
+    _require(sfb, torch.int32, "sfb")
+    _require(m_indices, torch.int32, "m_indices")
+    M, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K or c.shape != (M, N) or m_indices.shape != (M,):
+        raise ValueError("inconsistent grouped GEMM shapes")
+    if sfa.numel() != cdiv(cdiv(K, 128), 4) * cdiv(M, a_block_rows):
+        raise ValueError("sfa must hold ceil(K/512)*ceil(M/a_block_rows) int32")
+    if sfb.numel() != G * cdiv(cdiv(K, 128), 4) * cdiv(N, 128):
+        raise ValueError("sfb must hold G*ceil(K/512)*ceil(N/128) int32")
+    _check(lib.dg_fp8_grouped_gemm_contig_ue8m0(_ptr(c), _ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb),
+                                                a_block_rows, _ptr(m_indices), G, M, N, K,
+                                                _stream(stream)), "dg_fp8_grouped_gemm_contig_ue8m0")
+
+
 def dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups: int, max_m: int, N: int,
                                               K: int) -> int:
     return lib.dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups, max_m, N, K)
@@ -488,6 +514,7 @@ __all__ = [
     "dg_fp8_gemm_nt_epilogue", "EPILOGUES", "dg_transpose_fp8", "dg_fp8_gemm_workspace_bytes",
     "dg_fp8_gemm", "LAYOUTS", "dg_fp8_grouped_gemm_k", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
     "dg_fp8_grouped_gemm_masked", "dg_fp8_grouped_gemm_masked_workspace_bytes",
+    "dg_fp8_grouped_gemm_contig_ue8m0",
 ]
 # (the _epilogue C entry points are reached through the act / residual
 # arguments of dg_fp8_grouped_gemm_contig and dg_fp8_grouped_gemm_masked)

@@ -279,6 +279,24 @@ int dg_fp8_grouped_gemm_contig_epilogue(uint16_t* c, const uint8_t* a, const uin
   return from_hip(dg::launch_gemm_tiled(p, true, static_cast<hipStream_t>(stream)));
 }
 
+int dg_fp8_grouped_gemm_contig_ue8m0(uint16_t* c, const uint8_t* a, const uint8_t* b,
+                                     const int32_t* sfa, const int32_t* sfb, int a_block_rows,
+                                     const int32_t* m_indices, int num_groups, int64_t M,
+                                     int64_t N, int64_t K, void* stream) {
+  int st = check_gemm(c, a, b, reinterpret_cast<const float*>(sfa),
+                      reinterpret_cast<const float*>(sfb), a_block_rows, M, N, K);
+  if (st != DG_OK) return st;
+  if (!m_indices) return DG_ERR_NULL;
+  if (!aligned(m_indices, 4)) return DG_ERR_ALIGN;
+  if (num_groups < 1) return DG_ERR_UNSUPPORTED;
+  if (M % 128 != 0) return DG_ERR_SHAPE;
+  if ((int64_t)num_groups * N * K / num_groups != N * K) return DG_ERR_SHAPE;
+  dg::GemmProblem p{c, a, b, nullptr, nullptr, m_indices, num_groups, a_block_rows, M, N, K};
+  p.sfa = reinterpret_cast<const uint32_t*>(sfa);
+  p.sfb = reinterpret_cast<const uint32_t*>(sfb);
+  return from_hip(dg::launch_gemm_tiled_grouped_ue8m0(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t dg_fp8_grouped_gemm_masked_workspace_bytes(int num_groups, int64_t max_m, int64_t N,
                                                   int64_t K) {
   if (num_groups < 1 || max_m < 1 || N < 1 || K < 1) return 0;

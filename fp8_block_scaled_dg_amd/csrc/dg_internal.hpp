@@ -60,6 +60,9 @@ hipError_t launch_gemm_tiled(const GemmProblem& p, bool grouped, hipStream_t str
 hipError_t launch_gemm_tiled_kgrouped(const GemmProblem& p, hipStream_t stream);
 // Dense 256 x 256 tile kernel with UE8M0 scales applied by the scaled MFMA.
 hipError_t launch_gemm_tiled_ue8m0(const GemmProblem& p, hipStream_t stream);
+// Grouped (M-contiguous) ring kernel with UE8M0 scales: sfa as dense, sfb
+// [G][ceil(K/512)][ceil(N/128)].
+hipError_t launch_gemm_tiled_grouped_ue8m0(const GemmProblem& p, hipStream_t stream);
 
 // Skinny (small-M) kernel: workspace may be null (then no split-K).
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);

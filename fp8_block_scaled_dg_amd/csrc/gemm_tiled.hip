@@ -168,7 +168,7 @@ __device__ __forceinline__ void map_tile(const TiledArgs& p, bool grouped, int& 
 // when the workgroup has nothing more to do.
 __device__ __forceinline__ bool grouped_tile(const TiledArgs& p, int blk, int n0, int lane,
                                              int& m0, int& rows_end, const uint8_t*& bbase,
-                                             const float*& sbbase) {
+                                             const float*& sbbase, const uint32_t*& sfbbase) {
   m0 = blk * 128;
   const int g = p.m_indices[m0];
   if (g < 0 || g >= p.num_groups) {
@@ -203,6 +203,7 @@ __device__ __forceinline__ bool grouped_tile(const TiledArgs& p, int blk, int n0
   rows_end = m0 + (pair ? 256 : 128);
   bbase += (int64_t)g * p.N * p.K;
   sbbase += (int64_t)g * p.nkb * p.sb_stride;
+  sfbbase += (int64_t)g * ((p.nkb + 3) / 4) * p.sb_stride;  // UE8M0: four K blocks per word
   return true;
 }
 
@@ -281,8 +282,9 @@ gemm_tiled_kernel(TiledArgs p) {
 
   const uint8_t* bbase = p.b;
   const float* sbbase = p.sb;
+  const uint32_t* sfbbase = p.sfb;  // UE8M0 B exponents (the expert's, when grouped)
   if (GROUPED) {
-    if (!grouped_tile(p, tm, n0, lane, m0, rows_end, bbase, sbbase)) return;
+    if (!grouped_tile(p, tm, n0, lane, m0, rows_end, bbase, sbbase, sfbbase)) return;
   }
 
   TileLoader<BM, NW> lda;
@@ -322,7 +324,7 @@ gemm_tiled_kernel(TiledArgs p) {
   if constexpr (E8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ea_cur[i] = (int)(p.sfa[sa_idx[i]] & 0xFFu);
-    eb_cur = (int)(p.sfb[nb] & 0xFFu);
+    eb_cur = (int)(sfbbase[nb] & 0xFFu);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sa_cur[i] = p.sa[(int64_t)kb_begin * p.sa_stride + sa_idx[i]];
@@ -348,7 +350,7 @@ gemm_tiled_kernel(TiledArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         ea_nxt[i] = (int)((p.sfa[(int64_t)w * p.sa_stride + sa_idx[i]] >> sh) & 0xFFu);
-      eb_nxt = (int)((p.sfb[(int64_t)w * p.sb_stride + nb] >> sh) & 0xFFu);
+      eb_nxt = (int)((sfbbase[(int64_t)w * p.sb_stride + nb] >> sh) & 0xFFu);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sa_nxt[i] = p.sa[(int64_t)kn * p.sa_stride + sa_idx[i]];
@@ -520,8 +522,9 @@ gemm_ring_kernel(TiledArgs p) {
   int rows_end = p.M;
   const uint8_t* bbase = p.b;
   const float* sbbase = p.sb;
+  const uint32_t* sfbbase = p.sfb;  // UE8M0 B exponents (the expert's, when grouped)
   if (GROUPED) {
-    if (!grouped_tile(p, tm, n0, lane, m0, rows_end, bbase, sbbase)) return;
+    if (!grouped_tile(p, tm, n0, lane, m0, rows_end, bbase, sbbase, sfbbase)) return;
   }
 
   TileLoader<BM, NW> lda;
@@ -661,7 +664,7 @@ gemm_ring_kernel(TiledArgs p) {
 
 template <bool RING, int A_BLK, bool GROUPED, bool E8 = false, bool KG = false>
 hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
-  static_assert(!(E8 && (RING || GROUPED)), "UE8M0 scales: dense two-stage kernel only");
+  static_assert(!(E8 && RING), "UE8M0 scales: two-stage kernel only");
   static_assert(!(KG && (RING || GROUPED || E8)), "K-grouped: dense two-stage kernel only");
   TiledArgs p;
   p.c = q.c; p.a = q.a; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
@@ -677,7 +680,7 @@ hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   p.tiles_n = (int)((q.N + BN - 1) / BN);
   p.group_m = 4;
   const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n) * (KG ? (unsigned)q.num_groups : 1u);
-  if (RING)
+  if constexpr (RING)
     hipLaunchKernelGGL((gemm_ring_kernel<A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream, p);
   else
     hipLaunchKernelGGL((gemm_tiled_kernel<256, A_BLK, GROUPED, E8, KG>), dim3(grid), dim3(512), 0,
@@ -715,6 +718,14 @@ hipError_t launch_gemm_tiled(const GemmProblem& q, bool grouped, hipStream_t str
 hipError_t launch_gemm_tiled_kgrouped(const GemmProblem& q, hipStream_t stream) {
   return q.a_block_rows == 1 ? launch_one<false, 1, false, false, true>(q, stream)
                              : launch_one<false, 128, false, false, true>(q, stream);
+}
+
+// Grouped with UE8M0 scales: the two-stage kernel (the grouped ring kernel
+// has no UE8M0 form; with the exponent registers on top of its five-slot
+// pipeline state it would not fit the register file without spills).
+hipError_t launch_gemm_tiled_grouped_ue8m0(const GemmProblem& q, hipStream_t stream) {
+  return q.a_block_rows == 1 ? launch_one<false, 1, true, true>(q, stream)
+                             : launch_one<false, 128, true, true>(q, stream);
 }
 
 hipError_t launch_gemm_tiled_ue8m0(const GemmProblem& q, hipStream_t stream) {

@@ -287,6 +287,22 @@ int dg_fp8_grouped_gemm_contig_epilogue(uint16_t *c, const uint8_t *a, const uin
                                         void *stream);
 
 /*
+ * Grouped GEMM, experts contiguous along M, with power-of-two (UE8M0) block
+ * scales [D s3.1: UE8M0 scales, four per int32; s2.3, s3.2, s3.3: grouped
+ * MoE GEMM].  As dg_fp8_grouped_gemm_contig with the scale arrays of
+ * dg_fp8_gemm_nt_ue8m0:
+ *   sfa : int32 [ceil(K/512)][ceil(M/a_block_rows)];
+ *   sfb : int32 [num_groups][ceil(K/512)][ceil(N/128)] (per expert as for the
+ *         dense call).
+ * Padding rows are written as zeros.  Requirements and errors as
+ * dg_fp8_grouped_gemm_contig.  Deterministic.
+ */
+int dg_fp8_grouped_gemm_contig_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                                     const int32_t *sfa, const int32_t *sfb, int a_block_rows,
+                                     const int32_t *m_indices, int num_groups, int64_t M,
+                                     int64_t N, int64_t K, void *stream);
+
+/*
  * Grouped GEMM, masked layout [D s2.3, s3.2: expert weights batched in one
  * grouped call].  The layout is a reading for decode-time MoE, where each
  * expert's token count is known only on the device: every expert has a fixed

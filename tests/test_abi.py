@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
                  "dg_quantize_fp8_block_ue8m0", "dg_fp8_gemm_nt_ue8m0", "dg_fp8_gemm_nt_epilogue",
                  "dg_transpose_fp8", "dg_fp8_gemm", "dg_fp8_gemm_workspace_bytes",
                  "dg_fp8_grouped_gemm_k", "dg_fp8_grouped_gemm_masked",
-                 "dg_fp8_grouped_gemm_masked_workspace_bytes"):
+                 "dg_fp8_grouped_gemm_masked_workspace_bytes", "dg_fp8_grouped_gemm_contig_ue8m0",
+                 "dg_fp8_grouped_gemm_contig_epilogue", "dg_fp8_grouped_gemm_masked_epilogue"):
         assert need in names
 
 
@@ -230,3 +231,14 @@ def test_grouped_epilogue_validation(dg):
         return lib.dg_fp8_grouped_gemm_masked_epilogue(P, P, P, P, P, 1, MI, 8, 16, 512, 512, act,
                                                        res, None, 0, None)
     assert me(act=7) == 3 and me(res=P1) == 4
+
+
+def test_grouped_ue8m0_validation(dg):
+    lib = dg.lib
+    MI = ctypes.c_void_p(0x10000)
+
+    def gu(mi=MI, G=4, M=256, K=512, br=1):
+        return lib.dg_fp8_grouped_gemm_contig_ue8m0(P, P, P, P, P, br, mi, G, M, 512, K, None)
+    assert gu(mi=None) == 1 and gu(G=0) == 3 and gu(br=7) == 3
+    assert gu(M=200) == 2 and gu(K=100) == 2
+    assert gu(mi=ctypes.c_void_p(0x10002)) == 4

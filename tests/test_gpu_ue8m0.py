@@ -210,3 +210,53 @@ def test_gemm_ue8m0_small_m_extreme_exponents(dg, orc):
             torch.cuda.synchronize()
             ref = orc.gemm_nt(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), a_block_rows=1)
             assert_close(bf16_to_f64(c), ref, what="ue8m0 extreme %dx%dx%d" % (M, N, K))
+
+
+def grouped_ue8m0_operands(orc, tokens, G, N, K, br, seed):
+    r = datagen.moe_routing(tokens, G, min(2, G), align=128, seed=seed)
+    mi = r["m_indices"]
+    a = datagen.gather_rows(datagen.normal((tokens, K), 1.0, seed=seed, stream=1), r["row_token"])
+    qa, ea = orc.quantize_ue8m0(a, br)
+    w = datagen.normal((G * N, K), 0.02, seed=seed, stream=2)
+    qb = np.empty((G, N, K), np.uint8)
+    ebs = []
+    for e in range(G):
+        qb[e], eb = orc.quantize_ue8m0(w[e * N:(e + 1) * N], 128)
+        ebs.append(eb)
+    return qa, ea, qb, ebs, mi
+
+
+@pytest.mark.parametrize("br", [1, 128])
+@pytest.mark.parametrize("tokens,G,N,K", [(100, 3, 264, 640), (300, 4, 512, 1152), (64, 8, 136, 128)])
+def test_grouped_gemm_ue8m0(dg, orc, tokens, G, N, K, br):
+    """Grouped M-contiguous GEMM with UE8M0 scales (pzsr.cn DeepGEMM page
+    s3.1, s3.2): against the oracle's grouped FP64 product with the
+    exponents as FP32 powers of two; padding rows exact zeros; K-block counts
+    that leave partial exponent words."""
+    qa, ea, qb, ebs, mi = grouped_ue8m0_operands(orc, tokens, G, N, K, br, seed=tokens + G)
+    M = qa.shape[0]
+    sfb = np.stack([orc.pack_ue8m0(eb) for eb in ebs])
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_grouped_gemm_contig_ue8m0(c, dev(qa), dev(qb), dev(orc.pack_ue8m0(ea)), dev(sfb), br,
+                                        dev(mi))
+    torch.cuda.synchronize()
+    got = bf16_to_f64(c)
+    real = mi >= 0
+    assert np.all(got[~real] == 0.0)
+    sb = np.stack([orc.ue8m0_scales(eb) for eb in ebs])
+    ref = orc.grouped_gemm_contig(qa, orc.ue8m0_scales(ea), qb, sb, mi, a_block_rows=br)
+    assert_close(got[real], ref[real], what="grouped ue8m0 %d/%d/%d/%d/%d" % (tokens, G, N, K, br))
+
+
+def test_grouped_gemm_ue8m0_one_expert_equals_dense(dg, orc):
+    qa, ea, qb, ebs, mi = grouped_ue8m0_operands(orc, 256, 1, 512, 1024, 1, seed=41)
+    M, N = qa.shape[0], qb.shape[1]
+    sfa = dev(orc.pack_ue8m0(ea))
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_grouped_gemm_contig_ue8m0(c, dev(qa), dev(qb), sfa,
+                                        dev(orc.pack_ue8m0(ebs[0])[None]), 1, dev(mi))
+    cd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm_nt_ue8m0(cd, dev(qa), dev(qb[0]), sfa, dev(orc.pack_ue8m0(ebs[0])), 1)
+    torch.cuda.synchronize()
+    real = mi >= 0
+    assert np.array_equal(bf16_to_f64(c)[real], bf16_to_f64(cd)[real])
