@@ -146,3 +146,31 @@ def test_graph_masked_grouped(dg, orc):
     A, B, SA, SB = dev(qa), dev(qb), dev(sa), dev(sb)
     check_graph(lambda: [torch.zeros((G, max_m, N), dtype=torch.bfloat16, device="cuda")],
                 lambda o: dg.dg_fp8_grouped_gemm_masked(o[0], A, B, SA, SB, 1, mm, workspace=ws))
+
+
+def test_graph_grouped_epilogue_and_ue8m0(dg, orc):
+    G, N, K = 4, 512, 640
+    r = datagen.moe_routing(200, G, 2, align=128, seed=3)
+    mi = r["m_indices"]
+    a = datagen.gather_rows(datagen.normal((200, K), 1.0, seed=3, stream=1), r["row_token"])
+    M = mi.shape[0]
+    qa, sa = orc.quantize(a, 1)
+    qa8, ea = orc.quantize_ue8m0(a, 1)
+    w = datagen.normal((G * N, K), 0.02, seed=3, stream=2)
+    qb = np.empty((G, N, K), np.uint8)
+    sb = np.empty((G, K // 128, N // 128), np.float32)
+    qb8 = np.empty((G, N, K), np.uint8)
+    sfb = []
+    for e in range(G):
+        qb[e], sb[e] = orc.quantize(w[e * N:(e + 1) * N], 128)
+        qb8[e], eb = orc.quantize_ue8m0(w[e * N:(e + 1) * N], 128)
+        sfb.append(orc.pack_ue8m0(eb))
+    A, B, SA, SB, MI = dev(qa), dev(qb), dev(sa), dev(sb), dev(mi)
+    res = torch.randn((M, N // 2), device="cuda").to(torch.bfloat16)
+    check_graph(bf16(M, N // 2),
+                lambda o: dg.dg_fp8_grouped_gemm_contig(o[0], A, B, SA, SB, 1, MI, act="swiglu",
+                                                        residual=res))
+    A8, B8 = dev(qa8), dev(qb8)
+    SFA, SFB = dev(orc.pack_ue8m0(ea)), dev(np.stack(sfb))
+    check_graph(bf16(M, N),
+                lambda o: dg.dg_fp8_grouped_gemm_contig_ue8m0(o[0], A8, B8, SFA, SFB, 1, MI))
