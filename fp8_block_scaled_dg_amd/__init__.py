@@ -86,6 +86,9 @@ def _load():
     lib.dg_fp8_grouped_gemm_contig_ue8m0.restype = i32
     lib.dg_fp8_grouped_gemm_contig_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
                                                      i64, vp]
+    lib.dg_fp8_grouped_gemm_masked_ue8m0.restype = i32
+    lib.dg_fp8_grouped_gemm_masked_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
+                                                     i64, vp, ctypes.c_size_t, vp]
     lib.dg_fp8_grouped_gemm_masked.restype = i32
     lib.dg_fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp,
                                                ctypes.c_size_t, vp]
@@ -425,6 +428,30 @@ def dg_fp8_grouped_gemm_contig_ue8m0(c, a, b, sfa, sfb, a_block_rows: int, m_ind
                                                 _stream(stream)), "dg_fp8_grouped_gemm_contig_ue8m0")
 
 
+def dg_fp8_grouped_gemm_masked_ue8m0(c, a, b, sfa, sfb, a_block_rows: int, masked_m,
+                                     workspace=None, stream=None) -> None:
+    """Masked grouped with packed UE8M0 scales: sfa int32
+    [G, ceil(K/512), ceil(max_m/br)], sfb int32 [G, ceil(K/512), ceil(N/128)]."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sfa, torch.int32, "sfa")
+    _require(sfb, torch.int32, "sfb")
+    _require(masked_m, torch.int32, "masked_m")
+    G, max_m, K = a.shape
+    Gb, N, Kb = b.shape
+    if Gb != G or Kb != K or c.shape != (G, max_m, N) or masked_m.shape != (G,):
+        raise ValueError("inconsistent masked grouped GEMM shapes")
+    if sfa.numel() != G * cdiv(cdiv(K, 128), 4) * cdiv(max_m, a_block_rows):
+        raise ValueError("sfa must hold G*ceil(K/512)*ceil(max_m/a_block_rows) int32")
+    if sfb.numel() != G * cdiv(cdiv(K, 128), 4) * cdiv(N, 128):
+        raise ValueError("sfb must hold G*ceil(K/512)*ceil(N/128) int32")
+    _check(lib.dg_fp8_grouped_gemm_masked_ue8m0(_ptr(c), _ptr(a), _ptr(b), _ptr(sfa), _ptr(sfb),
+                                                a_block_rows, _ptr(masked_m), G, max_m, N, K,
+                                                _ptr(workspace), _workspace_bytes(workspace),
+                                                _stream(stream)), "dg_fp8_grouped_gemm_masked_ue8m0")
+
+
 def dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups: int, max_m: int, N: int,
                                               K: int) -> int:
     return lib.dg_fp8_grouped_gemm_masked_workspace_bytes(num_groups, max_m, N, K)
@@ -514,7 +541,7 @@ __all__ = [
     "dg_fp8_gemm_nt_epilogue", "EPILOGUES", "dg_transpose_fp8", "dg_fp8_gemm_workspace_bytes",
     "dg_fp8_gemm", "LAYOUTS", "dg_fp8_grouped_gemm_k", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
     "dg_fp8_grouped_gemm_masked", "dg_fp8_grouped_gemm_masked_workspace_bytes",
-    "dg_fp8_grouped_gemm_contig_ue8m0",
+    "dg_fp8_grouped_gemm_contig_ue8m0", "dg_fp8_grouped_gemm_masked_ue8m0",
 ]
 # (the _epilogue C entry points are reached through the act / residual
 # arguments of dg_fp8_grouped_gemm_contig and dg_fp8_grouped_gemm_masked)

@@ -297,6 +297,35 @@ int dg_fp8_grouped_gemm_contig_ue8m0(uint16_t* c, const uint8_t* a, const uint8_
   return from_hip(dg::launch_gemm_tiled_grouped_ue8m0(p, static_cast<hipStream_t>(stream)));
 }
 
+int dg_fp8_grouped_gemm_masked_ue8m0(uint16_t* c, const uint8_t* a, const uint8_t* b,
+                                     const int32_t* sfa, const int32_t* sfb, int a_block_rows,
+                                     const int32_t* masked_m, int num_groups, int64_t max_m,
+                                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  int st = check_gemm(c, a, b, reinterpret_cast<const float*>(sfa),
+                      reinterpret_cast<const float*>(sfb), a_block_rows, max_m, N, K);
+  if (st != DG_OK) return st;
+  if (!masked_m) return DG_ERR_NULL;
+  if (!aligned(masked_m, 4)) return DG_ERR_ALIGN;
+  if (num_groups < 1) return DG_ERR_UNSUPPORTED;
+  if (max_m > INT64_MAX / K / num_groups || max_m > INT64_MAX / N / num_groups)
+    return DG_ERR_SHAPE;
+  if (dg::skinny_masked_grid(num_groups, max_m, N, K) > INT32_MAX) return DG_ERR_SHAPE;
+  if (workspace != nullptr && workspace_bytes > 0) {
+    if (workspace_bytes < dg::skinny_masked_workspace_bytes(num_groups, max_m, N, K))
+      return DG_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DG_ERR_ALIGN;
+  } else {
+    workspace = nullptr;
+    workspace_bytes = 0;
+  }
+  dg::GemmProblem p{c, a, b, nullptr, nullptr, nullptr, num_groups, a_block_rows, max_m, N, K};
+  p.sfa = reinterpret_cast<const uint32_t*>(sfa);
+  p.sfb = reinterpret_cast<const uint32_t*>(sfb);
+  return from_hip(dg::launch_gemm_skinny_masked(p, masked_m, max_m, workspace, workspace_bytes,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t dg_fp8_grouped_gemm_masked_workspace_bytes(int num_groups, int64_t max_m, int64_t N,
                                                   int64_t K) {
   if (num_groups < 1 || max_m < 1 || N < 1 || K < 1) return 0;

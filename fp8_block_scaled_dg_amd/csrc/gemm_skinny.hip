@@ -106,7 +106,7 @@ template <int MP, int F, bool AF32 = false, bool E8 = false, int NS = 3, bool MA
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   static_assert(!AF32 || MP == 16, "in-kernel quantisation covers up to 16 rows");
   static_assert(!(AF32 && E8), "in-kernel quantisation uses FP32 scales");
-  static_assert(!(MASKED && (AF32 || E8)), "masked layout: E4M3 A with FP32 scales");
+  static_assert(!(MASKED && AF32), "masked layout: E4M3 A");
   constexpr int BNT = 64 * F;                     // B rows per workgroup (F fragments per wave)
   constexpr int MPE = MP < 32 ? 32 : MP;          // A rows staged (>= 4 DMA instructions)
   constexpr int B_BYTES = BNT * BK;               // 8 or 16 KB
@@ -154,6 +154,11 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
     p.sa += (int64_t)g * p.nkb * p.sa_stride + (p.a_block_rows == 1 ? r0 : r0 / 128);
     p.b += (int64_t)g * p.N * p.K;
     p.sb += (int64_t)g * p.nkb * p.sb_stride;
+    if constexpr (E8) {  // UE8M0 words: four K blocks each, per-group arrays
+      const int64_t nw = (p.nkb + 3) / 4;
+      p.sfa += g * nw * p.sa_stride + (p.a_block_rows == 1 ? r0 : r0 / 128);
+      p.sfb += g * nw * p.sb_stride;
+    }
     p.c += row0 * p.epi.ldc;  // (N / 2 columns with SwiGLU)
     if (p.epi.res) p.epi.res += row0 * p.epi.ldc;
     if (p.S > 1) p.partials += row0 * p.N;
@@ -643,14 +648,21 @@ MaskedPlan plan_masked(int num_groups, int64_t max_m, int64_t N, int64_t K) {
   return m;
 }
 
-template <int MP>
+template <int MP, bool E8>
 void launch_masked_mp(const SkinnyArgs& p, int bn, unsigned grid, hipStream_t stream) {
   if (bn == 64)
-    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 1, false, false, 3, true>), dim3(grid), dim3(256),
-                       0, stream, p);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 1, false, E8, 3, true>), dim3(grid), dim3(256), 0,
+                       stream, p);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 2, false, false, 3, true>), dim3(grid), dim3(256),
-                       0, stream, p);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 2, false, E8, 3, true>), dim3(grid), dim3(256), 0,
+                       stream, p);
+}
+
+template <bool E8>
+void launch_masked(const SkinnyArgs& p, int mp, int bn, unsigned grid, hipStream_t stream) {
+  if (mp == 16) launch_masked_mp<16, E8>(p, bn, grid, stream);
+  else if (mp == 32) launch_masked_mp<32, E8>(p, bn, grid, stream);
+  else launch_masked_mp<64, E8>(p, bn, grid, stream);
 }
 
 }  // namespace
@@ -671,7 +683,7 @@ hipError_t launch_gemm_skinny_masked(const GemmProblem& q, const int32_t* masked
   const MaskedPlan m = plan_masked(q.num_groups, max_m, q.N, q.K);
   SkinnyArgs p;
   p.c = q.c; p.a = q.a; p.af = nullptr; p.b = q.b; p.sa = q.sa; p.sb = q.sb;
-  p.sfa = nullptr; p.sfb = nullptr;
+  p.sfa = q.sfa; p.sfb = q.sfb;  // UE8M0 words in place of sa / sb, or null
   p.epi = resolved_epilogue(q);
   p.a_block_rows = q.a_block_rows;
   p.M = 0;  // per workgroup: the valid rows of its chunk
@@ -691,9 +703,8 @@ hipError_t launch_gemm_skinny_masked(const GemmProblem& q, const int32_t* masked
   p.chunks = m.chunks;
   p.tiles = m.tiles;
   const unsigned grid = (unsigned)((int64_t)q.num_groups * m.chunks * m.tiles * S);
-  if (m.mp == 16) launch_masked_mp<16>(p, m.bn, grid, stream);
-  else if (m.mp == 32) launch_masked_mp<32>(p, m.bn, grid, stream);
-  else launch_masked_mp<64>(p, m.bn, grid, stream);
+  if (q.sfa) launch_masked<true>(p, m.mp, m.bn, grid, stream);
+  else launch_masked<false>(p, m.mp, m.bn, grid, stream);
   return hipGetLastError();
 }
 

@@ -348,6 +348,19 @@ int dg_fp8_grouped_gemm_masked_epilogue(uint16_t *c, const uint8_t *a, const uin
                                         int64_t N, int64_t K, int act, const uint16_t *residual,
                                         void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * dg_fp8_grouped_gemm_masked with power-of-two (UE8M0) block scales [D s3.1]:
+ *   sfa : int32 [num_groups][ceil(K/512)][ceil(max_m/a_block_rows)];
+ *   sfb : int32 [num_groups][ceil(K/512)][ceil(N/128)]
+ * (each group's words as for dg_fp8_gemm_nt_ue8m0).  Everything else,
+ * including the workspace size query, as dg_fp8_grouped_gemm_masked.
+ */
+int dg_fp8_grouped_gemm_masked_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                                     const int32_t *sfa, const int32_t *sfb, int a_block_rows,
+                                     const int32_t *masked_m, int num_groups, int64_t max_m,
+                                     int64_t N, int64_t K, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

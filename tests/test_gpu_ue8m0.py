@@ -260,3 +260,41 @@ def test_grouped_gemm_ue8m0_one_expert_equals_dense(dg, orc):
     torch.cuda.synchronize()
     real = mi >= 0
     assert np.array_equal(bf16_to_f64(c)[real], bf16_to_f64(cd)[real])
+
+
+@pytest.mark.parametrize("ws", [False, True])
+@pytest.mark.parametrize("br", [1, 128])
+def test_masked_grouped_gemm_ue8m0(dg, orc, br, ws):
+    """Masked grouped layout with UE8M0 scales: valid rows within the GEMM
+    tolerance of the oracle's masked product (exponents as FP32 powers of
+    two), rows past the counts untouched; K-block count leaving partial
+    exponent words; with and without the split-K workspace."""
+    G, max_m, N, K = 6, 40, 1024, 4224
+    mm = np.array([40, 0, 9, 33, 1, 17], np.int32)
+    qa = np.empty((G, max_m, K), np.uint8)
+    qb = np.empty((G, N, K), np.uint8)
+    eas, ebs = [], []
+    for g in range(G):
+        qa[g], ea = orc.quantize_ue8m0(datagen.normal((max_m, K), 1.0, seed=g, stream=5), br)
+        qb[g], eb = orc.quantize_ue8m0(datagen.normal((N, K), 0.02, seed=g, stream=6), 128)
+        eas.append(ea)
+        ebs.append(eb)
+    sfa = np.stack([orc.pack_ue8m0(e) for e in eas])
+    sfb = np.stack([orc.pack_ue8m0(e) for e in ebs])
+    c = torch.full((G, max_m, N), 0x4B1D, dtype=torch.int16, device="cuda")
+    w = None
+    if ws:
+        nb = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, max_m, N, K)
+        assert nb > 0
+        w = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dg.dg_fp8_grouped_gemm_masked_ue8m0(c, dev(qa), dev(qb), dev(sfa), dev(sfb), br, dev(mm),
+                                        workspace=w)
+    torch.cuda.synchronize()
+    bits = c.cpu().numpy().view(np.uint16)
+    got = bf16_to_f64(c)
+    sa = np.stack([orc.ue8m0_scales(e) for e in eas])
+    sb = np.stack([orc.ue8m0_scales(e) for e in ebs])
+    ref = orc.grouped_gemm_masked(qa, sa, qb, sb, mm, a_block_rows=br)
+    valid = ~np.isnan(ref)
+    assert np.all(bits[~valid] == 0x4B1D)
+    assert_close(got[valid], ref[valid], what="masked ue8m0 br=%d ws=%s" % (br, ws))
