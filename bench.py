@@ -363,7 +363,7 @@ class Decode:
                 M=M, N=N, K=K, qb=qb, sb=sb, a=a, copies=copies,
                 qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
                 sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
-                ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda"),
+                ws=torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda"),
                 c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         self.rot = max(it["copies"] for it in self.items)
         self.flops = sum(2.0 * it["M"] * it["N"] * it["K"] for it in self.items)
@@ -741,7 +741,7 @@ class Masked:
             ws_bytes = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, cap, N, K)
             self.items.append(dict(
                 G=G, cap=cap, N=N, K=K, qb=qb, sb=sb, qa=qa, sa=sa, mm=mm,
-                ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda"),
+                ws=torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda"),
                 c=torch.zeros((G, cap, N), dtype=torch.bfloat16, device="cuda")))
         self.flops = sum(2.0 * self.real_rows * it["N"] * it["K"] for it in self.items)
 

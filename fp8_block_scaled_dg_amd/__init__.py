@@ -26,7 +26,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libdg.so")
 
 DG_OK = 0
-ABI_VERSION = 1
+ABI_VERSION = 2
+# arrival-counter region at the start of every split-K workspace (dg.h)
+WORKSPACE_COUNTER_BYTES = 32768
 
 
 class DGError(RuntimeError):
@@ -154,6 +156,13 @@ def _workspace_bytes(workspace) -> int:
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     return workspace.numel() * workspace.element_size()
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    """A split-K workspace of at least nbytes (16 minimum), zero-filled: its
+    counter region must be zero before first use; every call leaves it zero,
+    so the tensor can be reused by later calls ordered after this one."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def cdiv(a: int, b: int) -> int:
@@ -541,7 +550,8 @@ __all__ = [
     "dg_fp8_gemm_nt_epilogue", "EPILOGUES", "dg_transpose_fp8", "dg_fp8_gemm_workspace_bytes",
     "dg_fp8_gemm", "LAYOUTS", "dg_fp8_grouped_gemm_k", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
     "dg_fp8_grouped_gemm_masked", "dg_fp8_grouped_gemm_masked_workspace_bytes",
-    "dg_fp8_grouped_gemm_contig_ue8m0", "dg_fp8_grouped_gemm_masked_ue8m0",
+    "dg_fp8_grouped_gemm_contig_ue8m0", "dg_fp8_grouped_gemm_masked_ue8m0", "alloc_workspace",
+    "WORKSPACE_COUNTER_BYTES",
 ]
 # (the _epilogue C entry points are reached through the act / residual
 # arguments of dg_fp8_grouped_gemm_contig and dg_fp8_grouped_gemm_masked)

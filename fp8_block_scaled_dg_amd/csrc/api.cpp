@@ -10,6 +10,9 @@
 
 namespace {
 
+static_assert(DG_WORKSPACE_COUNTER_BYTES == dg::kSplitkCounterBytes,
+              "counter region of dg.h and of the kernels");
+
 constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kU32 = 4294967295LL;
 
@@ -193,7 +196,12 @@ int dg_transpose_fp8(uint8_t* out, const uint8_t* in, int64_t rows, int64_t cols
 
 size_t dg_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int layout) {
   if (M < 1 || N < 1 || K < 1 || layout < DG_LAYOUT_NT || layout > DG_LAYOUT_TT) return 0;
-  return transpose_bytes(M, N, K, layout) + dg_fp8_gemm_nt_workspace_bytes(M, N, K);
+  const size_t nt = dg_fp8_gemm_nt_workspace_bytes(M, N, K);
+  if (layout == DG_LAYOUT_NT) return nt;
+  // split-K region (at least the counter region, which the transposes never
+  // touch) first, then the transposed copies
+  return (nt > DG_WORKSPACE_COUNTER_BYTES ? nt : DG_WORKSPACE_COUNTER_BYTES) +
+         transpose_bytes(M, N, K, layout);
 }
 
 int dg_fp8_gemm(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa, const float* sb,
@@ -203,6 +211,7 @@ int dg_fp8_gemm(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa
   if (layout == DG_LAYOUT_NT)
     return dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, M, N, K, workspace, workspace_bytes,
                           stream);
+  // every check, the NT GEMM's included, before the first launch
   int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
   if (st != DG_OK) return st;
   const bool a_t = layout == DG_LAYOUT_TN || layout == DG_LAYOUT_TT;  // A given [K][M]
@@ -210,18 +219,24 @@ int dg_fp8_gemm(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa
   if ((a_t && M % 16 != 0) || (b_n && N % 16 != 0)) return DG_ERR_SHAPE;
   if ((a_t && (K + 127) / 128 > kMaxGridY) || (b_n && (K + 127) / 128 > kMaxGridY))
     return DG_ERR_SHAPE;
+  const bool skinny = dg::skinny_applies(M, N, K);
+  if (!skinny && ((M + 255) / 256) * ((N + 255) / 256) > INT32_MAX) return DG_ERR_SHAPE;
   const size_t tb = transpose_bytes(M, N, K, layout);
-  if (!workspace || workspace_bytes < tb) return DG_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < DG_WORKSPACE_COUNTER_BYTES + tb) return DG_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return DG_ERR_ALIGN;
+  // split-K when the workspace also holds the plan's partials after the
+  // copies; otherwise the copies follow the (untouched) counter region
+  const size_t split = skinny ? dg::skinny_workspace_bytes(M, N, K) : 0;
+  const bool use_split = split > 0 && workspace_bytes >= split + tb;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  size_t used = use_split ? split : DG_WORKSPACE_COUNTER_BYTES;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* ak = a;
   const uint8_t* bk = b;
-  size_t used = 0;
   if (a_t) {
-    st = from_hip(dg::launch_transpose_u8(ws, a, K, M, s));  // [K][M] -> [M][K]
+    st = from_hip(dg::launch_transpose_u8(ws + used, a, K, M, s));  // [K][M] -> [M][K]
     if (st != DG_OK) return st;
-    ak = ws;
+    ak = ws + used;
     used += align16(M * K);
   }
   if (b_n) {
@@ -230,10 +245,8 @@ int dg_fp8_gemm(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa
     bk = ws + used;
     used += align16(N * K);
   }
-  // the rest of the workspace, if large enough, serves the small-M split-K plan
-  void* rest = workspace_bytes > used ? ws + used : nullptr;
-  return dg_fp8_gemm_nt(c, ak, bk, sa, sb, a_block_rows, M, N, K, rest,
-                        rest ? workspace_bytes - used : 0, stream);
+  return dg_fp8_gemm_nt(c, ak, bk, sa, sb, a_block_rows, M, N, K, use_split ? workspace : nullptr,
+                        use_split ? split : 0, stream);
 }
 
 int dg_fp8_grouped_gemm_k(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,

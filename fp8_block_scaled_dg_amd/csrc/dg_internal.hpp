@@ -39,7 +39,7 @@ struct GemmProblem {
   int a_block_rows;          // 1 or 128
   int64_t M, N, K;
   // power-of-two (UE8M0) scales, packed four K blocks per word, in place of
-  // sa / sb (dense tiled kernel only), else nullptr
+  // sa / sb (every kernel has a form that takes them), else nullptr
   const uint32_t* sfa = nullptr;
   const uint32_t* sfb = nullptr;
   Epilogue epi;
@@ -60,9 +60,15 @@ hipError_t launch_gemm_tiled(const GemmProblem& p, bool grouped, hipStream_t str
 hipError_t launch_gemm_tiled_kgrouped(const GemmProblem& p, hipStream_t stream);
 // Dense 256 x 256 tile kernel with UE8M0 scales applied by the scaled MFMA.
 hipError_t launch_gemm_tiled_ue8m0(const GemmProblem& p, hipStream_t stream);
-// Grouped (M-contiguous) ring kernel with UE8M0 scales: sfa as dense, sfb
-// [G][ceil(K/512)][ceil(N/128)].
+// Grouped (M-contiguous) two-stage tile kernel with UE8M0 scales: sfa as
+// dense, sfb [G][ceil(K/512)][ceil(N/128)].
 hipError_t launch_gemm_tiled_grouped_ue8m0(const GemmProblem& p, hipStream_t stream);
+
+// Split-K workspace of the small-M kernels: the first kSplitkCounterBytes
+// hold one arrival counter per tile (zero on entry, left zero by every call),
+// the partial tiles follow.  The region is the same for every shape, so one
+// workspace can serve calls of any shape in turn.
+constexpr size_t kSplitkCounterBytes = 32768;
 
 // Skinny (small-M) kernel: workspace may be null (then no split-K).
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);

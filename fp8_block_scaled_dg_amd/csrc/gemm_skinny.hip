@@ -25,10 +25,13 @@
 //  * Split-K when N/128 workgroups cannot fill the GPU: split s writes its
 //    FP32 partial tile to the caller's workspace, then the last split to
 //    arrive (device-scope counter) sums the S partials in split order and
-//    writes BF16, so the result does not depend on arrival order.  Counters
-//    live in a static device array that starts at zero and is reset by the
-//    reducing workgroup, so every call leaves it zeroed.  Two calls that
-//    overlap on one GPU (different streams) must not both use split-K.
+//    writes BF16, so the result does not depend on arrival order.  The
+//    arrival counters sit in the first kSplitkCounterBytes of the same
+//    workspace (one int per tile, a fixed region whatever the shape); the
+//    caller hands the workspace over zeroed once, and the reducing workgroup
+//    resets its counter, so every call leaves the region zeroed again.  The
+//    library keeps no state of its own: calls with distinct workspaces may
+//    overlap on one GPU.
 #include "dg_device.hpp"
 #include "dg_internal.hpp"
 
@@ -40,10 +43,8 @@ namespace {
 constexpr int BN = 128;
 constexpr int BK = 128;
 constexpr int kMaxNS = 8;          // deepest LDS ring (named slot arrays l0 .. l7)
-constexpr int kMaxCounters = 8192; // tiles: N up to 1M with 128-row tiles
+constexpr int kMaxCounters = (int)(kSplitkCounterBytes / 4);  // tiles: N up to 1M with 128-row tiles
 constexpr int kMaxSplits = 16;
-
-__device__ int g_splitk_counters[kMaxCounters];
 
 struct SkinnyArgs {
   uint16_t* c;
@@ -56,6 +57,7 @@ struct SkinnyArgs {
   const float* sa;
   const float* sb;
   float* partials;  // split s at partials + s * part_stride, row-major [.][N], when S > 1
+  int* counters;    // per-tile arrival counters (zero on entry, left zero), when S > 1
   int64_t part_stride;
   int a_block_rows;
   int M, N, K;
@@ -151,13 +153,14 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
     if (rows <= 0) return;  // uniform: before any barrier
     const int64_t row0 = (int64_t)g * p.max_m + r0;
     p.a += row0 * p.K;
-    p.sa += (int64_t)g * p.nkb * p.sa_stride + (p.a_block_rows == 1 ? r0 : r0 / 128);
     p.b += (int64_t)g * p.N * p.K;
-    p.sb += (int64_t)g * p.nkb * p.sb_stride;
     if constexpr (E8) {  // UE8M0 words: four K blocks each, per-group arrays
       const int64_t nw = (p.nkb + 3) / 4;
       p.sfa += g * nw * p.sa_stride + (p.a_block_rows == 1 ? r0 : r0 / 128);
       p.sfb += g * nw * p.sb_stride;
+    } else {
+      p.sa += (int64_t)g * p.nkb * p.sa_stride + (p.a_block_rows == 1 ? r0 : r0 / 128);
+      p.sb += (int64_t)g * p.nkb * p.sb_stride;
     }
     p.c += row0 * p.epi.ldc;  // (N / 2 columns with SwiGLU)
     if (p.epi.res) p.epi.res += row0 * p.epi.ldc;
@@ -409,7 +412,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
   __syncthreads();  // ... and so have those of every wave of the workgroup
   if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(&g_splitk_counters[tile], 1, __ATOMIC_RELAXED,
+    const int prev = __hip_atomic_fetch_add(&p.counters[tile], 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == p.S - 1);
   }
@@ -477,7 +480,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
     }
   });
   if (threadIdx.x == 0)  // leave the counter zeroed for the next call
-    __hip_atomic_store(&g_splitk_counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Optional override for tuning sweeps: DG_SKINNY_SPLITS=<S> (read once).
@@ -528,6 +531,16 @@ int choose_splits(int64_t M, int64_t N, int64_t K) {
   return (int)S;
 }
 
+// Workspace layout: the arrival counters (kSplitkCounterBytes, at a fixed
+// place so that calls of any shape can share one workspace), then the
+// partial tiles of the S splits.
+void set_split_workspace(SkinnyArgs& p, void* workspace) {
+  p.counters = static_cast<int*>(workspace);
+  p.partials = workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                    kSplitkCounterBytes)
+                         : nullptr;
+}
+
 }  // namespace
 
 bool skinny_applies(int64_t M, int64_t N, int64_t K) {
@@ -536,7 +549,7 @@ bool skinny_applies(int64_t M, int64_t N, int64_t K) {
 
 size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int S = choose_splits(M, N, K);
-  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+  return S > 1 ? kSplitkCounterBytes + (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, void* workspace,
@@ -559,7 +572,7 @@ hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, voi
   if (forced_splits() == 0 && S > p.nkb / 5) S = p.nkb / 5 > 1 ? p.nkb / 5 : 1;
   if (workspace == nullptr || workspace_bytes < skinny_workspace_bytes(q.M, q.N, q.K)) S = 1;
   p.S = S;
-  p.partials = static_cast<float*>(workspace);
+  set_split_workspace(p, workspace);
   p.part_stride = q.M * q.N;
   p.masked_m = nullptr;
   p.max_m = p.chunks = p.tiles = 0;
@@ -602,7 +615,7 @@ hipError_t launch_gemm_skinny(const GemmProblem& q, void* workspace, size_t work
   int S = choose_splits(q.M, q.N, q.K);
   if (workspace == nullptr || workspace_bytes < skinny_workspace_bytes(q.M, q.N, q.K)) S = 1;
   p.S = S;
-  p.partials = static_cast<float*>(workspace);
+  set_split_workspace(p, workspace);
   p.part_stride = q.M * q.N;
   p.masked_m = nullptr;
   p.max_m = p.chunks = p.tiles = 0;
@@ -669,7 +682,8 @@ void launch_masked(const SkinnyArgs& p, int mp, int bn, unsigned grid, hipStream
 
 size_t skinny_masked_workspace_bytes(int num_groups, int64_t max_m, int64_t N, int64_t K) {
   const MaskedPlan m = plan_masked(num_groups, max_m, N, K);
-  return m.S > 1 ? (size_t)m.S * (size_t)num_groups * (size_t)max_m * (size_t)N * sizeof(float)
+  return m.S > 1 ? kSplitkCounterBytes +
+                       (size_t)m.S * (size_t)num_groups * (size_t)max_m * (size_t)N * sizeof(float)
                  : 0;
 }
 
@@ -696,7 +710,7 @@ hipError_t launch_gemm_skinny_masked(const GemmProblem& q, const int32_t* masked
       workspace_bytes < skinny_masked_workspace_bytes(q.num_groups, max_m, q.N, q.K))
     S = 1;
   p.S = S;
-  p.partials = static_cast<float*>(workspace);
+  set_split_workspace(p, workspace);
   p.part_stride = (int64_t)q.num_groups * max_m * q.N;
   p.masked_m = masked_m;
   p.max_m = (int)max_m;

@@ -24,6 +24,17 @@
  *     K-block kb sits at scales[kb * n_row_blocks + rb] [Q s3.1: a separate
  *     array indexed by block, accessed contiguously].
  *   - Inputs must be finite.  Behaviour on NaN/Inf inputs is unspecified.
+ *   - Split-K workspaces (the optional `workspace` argument of the small-M
+ *     capable calls): the first DG_WORKSPACE_COUNTER_BYTES bytes hold one
+ *     arrival counter per output tile and must be ZERO when a workspace is
+ *     first used (allocate it zero-filled, or clear it once); every call
+ *     leaves them zero again when its work completes, and no call ever
+ *     writes anything else there, so one workspace can serve any sequence of
+ *     calls, of any shape, that are ordered on the device.  The rest of the
+ *     workspace need not be initialised and is clobbered.  Calls that may
+ *     run at the same time (e.g. on different streams) need distinct
+ *     workspaces; the library itself keeps no state between calls, so with
+ *     distinct workspaces every call is re-entrant.
  */
 #ifndef DG_H
 #define DG_H
@@ -35,7 +46,10 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 1
+#define DG_ABI_VERSION 2
+
+/* Size of the arrival-counter region at the start of a split-K workspace. */
+#define DG_WORKSPACE_COUNTER_BYTES 32768
 
 enum {
     DG_OK = 0,
@@ -92,8 +106,9 @@ int dg_quantize_fp8_block_ue8m0(uint8_t *q, int32_t *sf, const float *x,
 
 /*
  * Workspace bytes dg_fp8_gemm_nt can use for split-K on this shape (0 when
- * the chosen plan needs none).  Passing a smaller, non-NULL workspace is an
- * error; passing NULL/0 selects a plan that needs none.
+ * the chosen plan needs none; otherwise DG_WORKSPACE_COUNTER_BYTES plus the
+ * partial tiles).  Passing a smaller, non-NULL workspace is an error;
+ * passing NULL/0 selects a plan that needs none.
  */
 size_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -108,11 +123,9 @@ size_t dg_fp8_gemm_nt_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *   sb : FP32 [K/128][ceil(N/128)] (128x128 blocks).
  *   workspace / workspace_bytes: optional device scratch for split-K on
  *        small-M shapes (see dg_fp8_gemm_nt_workspace_bytes); may be NULL/0.
- *        Its contents need not be initialised and are clobbered.  A split-K
- *        plan also uses a library-owned array of per-tile arrival counters
- *        on the device, which every call leaves zeroed: two split-K calls
- *        that run at the same time on one GPU (different streams) race on
- *        it, so such calls must be ordered (or given no workspace).
+ *        16-byte aligned; its counter region must be zero on first use (see
+ *        the conventions above); calls running at the same time need
+ *        distinct workspaces.
  * Requirements: M >= 1; N >= 8, N % 8 == 0; K >= 128, K % 128 == 0;
  * M*K and N*K below 2^32 (byte offsets inside the kernels are 32-bit),
  * else DG_ERR_SHAPE.
@@ -133,7 +146,7 @@ int dg_fp8_gemm_nt(uint16_t *c, const uint8_t *a, const uint8_t *b,
  *   sfa : int32 [ceil(K/512)][ceil(M/a_block_rows)], packed as written by
  *         dg_quantize_fp8_block_ue8m0; sfb : int32 [ceil(K/512)][ceil(N/128)].
  *   workspace / workspace_bytes: optional split-K scratch for M <= 64, as
- *         for dg_fp8_gemm_nt (same size query, same counter rule).
+ *         for dg_fp8_gemm_nt (same size query, same workspace rules).
  * The kernel plan is dg_fp8_gemm_nt's (small-M kernels for M <= 64).
  * Deterministic.
  */
@@ -154,7 +167,7 @@ int dg_fp8_gemm_nt_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
  * quantiser would write, formed in registers and never stored.
  *   workspace / workspace_bytes: optional split-K scratch, as for
  *        dg_fp8_gemm_nt (size from dg_fp8_gemm_nt_workspace_bytes(M, N, K);
- *        same counter rule for calls that overlap on one GPU).
+ *        same workspace rules).
  * Requirements: 1 <= M <= DG_FUSED_A_MAX_M (small-batch decode); N >= 8,
  * N % 8 == 0; K >= 128, K % 128 == 0; N*K below 2^32; else DG_ERR_SHAPE.
  * Deterministic.
@@ -215,10 +228,14 @@ int dg_transpose_fp8(uint8_t *out, const uint8_t *in, int64_t rows, int64_t cols
  *            DG_LAYOUT_NN: a [M][K], b [K][N]
  *            DG_LAYOUT_TT: a [K][M], b [N][K]
  * Operands stored M- or N-major are first transposed into the workspace
- * (dg_transpose_fp8), then the NT kernels run.  workspace_bytes must be at
- * least dg_fp8_gemm_workspace_bytes(M, N, K, layout) minus the optional
- * split-K part (the transposed copies are required: DG_ERR_WORKSPACE
- * otherwise); whatever is left serves the small-M split-K plan.
+ * (dg_transpose_fp8), then the NT kernels run.  Workspace layout for TN, NN
+ * and TT: the split-K region of dg_fp8_gemm_nt first (at least its
+ * DG_WORKSPACE_COUNTER_BYTES counter region, zero on first use as for every
+ * workspace, never written by the transposes), then the transposed copies.
+ * dg_fp8_gemm_workspace_bytes(M, N, K, layout) is the full size (split-K
+ * included when the small-M plan uses it); DG_WORKSPACE_COUNTER_BYTES plus
+ * the transposed copies is the minimum (DG_ERR_WORKSPACE below that, with
+ * nothing enqueued), which runs the plan without split-K.
  * Requirements: those of dg_fp8_gemm_nt; M % 16 == 0 when A is [K][M],
  * N % 16 == 0 when B is [K][N]; unknown layout -> DG_ERR_UNSUPPORTED.
  */
@@ -318,9 +335,8 @@ int dg_fp8_grouped_gemm_contig_ue8m0(uint16_t *c, const uint8_t *a, const uint8_
  *              dg_fp8_gemm_nt with the group's scale arrays); the other rows
  *              are not written.
  *   workspace: optional split-K scratch, as for dg_fp8_gemm_nt; its size is
- *              dg_fp8_grouped_gemm_masked_workspace_bytes (0: none needed).
- *              A call that uses it must not overlap another split-K call on
- *              the same GPU.
+ *              dg_fp8_grouped_gemm_masked_workspace_bytes (0: none needed);
+ *              same workspace rules.
  * Requirements: those of dg_fp8_gemm_nt with M = max_m (max_m >= 1; N >= 8,
  * N % 8 == 0; K % 128 == 0; max_m*K and N*K below 2^32); 1 <= num_groups.
  * Rows are processed in chunks of up to 64 per workgroup, so B is streamed

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(dg):
 
 
 def test_abi_version_and_status_strings(dg):
-    assert dg.lib.dg_abi_version() == 1
+    assert dg.lib.dg_abi_version() == 2 == dg.ABI_VERSION
     for st in range(0, 7):
         assert dg.status_string(st) and dg.status_string(st) != "unknown status"
     assert dg.status_string(99) == "unknown status"
@@ -182,13 +182,20 @@ def test_layouts_transpose_and_k_grouped_validation(dg):
         return lib.dg_fp8_gemm(P, P, P, P, P, 128, M, N, K, layout, ws, wsb, None)
     assert gl(layout=4) == 3 and gl(layout=-1) == 3
     need = dg.dg_fp8_gemm_workspace_bytes(256, 256, 256, "tn")
-    assert need >= 2 * 256 * 256
+    # the counter region first (never written by the transposes), then the copies
+    assert need == dg.WORKSPACE_COUNTER_BYTES + 2 * 256 * 256
     assert gl() == 5                                   # transposed operands need a workspace
     assert gl(ws=P, wsb=16) == 5
+    assert gl(ws=P, wsb=2 * 256 * 256) == 5            # copies without the counter region
     assert gl(ws=P1, wsb=need) == 4
     assert gl(M=264, ws=P, wsb=1 << 30) == 2            # A given [K][M] needs M % 16 == 0
     assert dg.dg_fp8_gemm_workspace_bytes(256, 256, 256, "nt") == \
         dg.dg_fp8_gemm_nt_workspace_bytes(256, 256, 256)
+    # small M: the split-K region (counters + partials) ahead of the copies
+    nt = dg.dg_fp8_gemm_nt_workspace_bytes(16, 4096, 4096)
+    assert nt > dg.WORKSPACE_COUNTER_BYTES
+    assert dg.dg_fp8_gemm_workspace_bytes(16, 4096, 4096, "nn") == nt + 4096 * 4096
+    assert dg.dg_fp8_gemm_workspace_bytes(16, 4096, 4096, "tt") == nt + 16 * 4096
 
     def gk(ko=P, G=2, M=256, N=256, K=256):
         return lib.dg_fp8_grouped_gemm_k(P, P, P, P, P, 128, ko, G, M, N, K, None)

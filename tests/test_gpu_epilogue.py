@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import datagen
-from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu, oracle_gemm_rows, tile_points
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,7 @@ def bf16_bits(x):
 def run(dg, qa, sa, qb, sb, act, residual=None, in_place=False, ws=False):
     M, N = qa.shape[0], qb.shape[0]
     n_out = N // 2 if act == "swiglu" else N
-    c = torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda")
+    c = torch.full((M, n_out), float("nan"), dtype=torch.bfloat16, device="cuda")
     res = None
     if residual is not None:
         res = torch.from_numpy(residual.view(np.int16)).cuda().view(torch.bfloat16)
@@ -54,7 +54,7 @@ def run(dg, qa, sa, qb, sb, act, residual=None, in_place=False, ws=False):
     w = None
     if ws:
         nb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, qa.shape[1])
-        w = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        w = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
     dg.dg_fp8_gemm_nt_epilogue(c, dev(qa), dev(qb), dev(sa), dev(sb), 1, act=act, residual=res,
                                workspace=w)
     torch.cuda.synchronize()
@@ -82,6 +82,20 @@ def test_epilogue_residual(dg, orc, M, N, K, ws, act, in_place):
     assert_close(c, ref, what="%s+res %dx%dx%d in_place=%s" % (act, M, N, K, in_place))
 
 
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_epilogue_tile_order_full_compare(dg, orc, act):
+    """6 x 10 tiles of 256 x 256 (more than one 4-row band, every XCD's run
+    of tiles, ragged edges) with the epilogue and a residual, in full."""
+    M, N, K = 1300, 2312, 256
+    qa, sa, qb, sb = operands(orc, M, N, K, seed=17)
+    n_out = N // 2 if act == "swiglu" else N
+    r = bf16_bits(datagen.normal((M, n_out), 0.5, seed=3, stream=7))
+    ref = orc.epilogue(oracle_gemm_rows(orc, qa, sa, qb, sb, 1), act, residual=r)
+    c = run(dg, qa, sa, qb, sb, act, residual=r)
+    assert torch.isfinite(c).all()
+    assert_close(bf16_to_f64(c), ref, what="%s+res tile order" % act)
+
+
 @pytest.mark.parametrize("M,N,K,ws", SHAPES)
 def test_epilogue_none_equals_plain_gemm(dg, orc, M, N, K, ws):
     qa, sa, qb, sb = operands(orc, M, N, K, seed=5)
@@ -89,7 +103,7 @@ def test_epilogue_none_equals_plain_gemm(dg, orc, M, N, K, ws):
     c2 = torch.empty_like(c1)
     w = None
     if ws:
-        w = torch.empty(max(dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
+        w = torch.zeros(max(dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K), 16), dtype=torch.uint8,
                         device="cuda")
     dg.dg_fp8_gemm_nt(c2, dev(qa), dev(qb), dev(sa), dev(sb), 1, workspace=w)
     torch.cuda.synchronize()
@@ -102,9 +116,11 @@ def test_swiglu_full_size_sampled(dg, orc):
     M, N, K = 2048, 22016, 4096
     qa, sa, qb, sb = operands(orc, M, N, K, seed=1)
     c = run(dg, qa, sa, qb, sb, "swiglu")
+    assert torch.isfinite(c).all()                  # every element written (NaN prefill)
     g = np.random.default_rng(4)
-    pm = np.concatenate([g.integers(0, M, 800), np.full(N // 2, M - 1)])
-    pj = np.concatenate([g.integers(0, N // 2, 800), np.arange(N // 2)])
+    tm, tj = tile_points(M, N // 2, 256, 128, g)   # a 256 x 256 tile gives 128 outputs per row
+    pm = np.concatenate([g.integers(0, M, 800), np.full(N // 2, M - 1), tm])
+    pj = np.concatenate([g.integers(0, N // 2, 800), np.arange(N // 2), tj])
     assert pm.max() < M and pj.max() < N // 2
     gate = orc.gemm_nt_points(qa, sa, qb, sb, pm, 2 * pj, a_block_rows=1)
     up = orc.gemm_nt_points(qa, sa, qb, sb, pm, 2 * pj + 1, a_block_rows=1)

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import datagen
-from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu, tile_points
 
 pytestmark = pytest.mark.gpu
 
@@ -29,12 +29,12 @@ def dg():
 
 def workspace(dg, M, N, K):
     n = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda") if n else None
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device="cuda") if n else None
 
 
 def fused(dg, a, qb, sb, ws=None):
     M, N = a.shape[0], qb.shape[0]
-    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     dg.dg_fp8_gemm_nt_fused_a(c, dev(a), dev(qb), dev(sb), workspace=ws)
     torch.cuda.synchronize()
     return c
@@ -123,11 +123,13 @@ def test_fused_decode_shapes_sampled(dg, orc, M, N, K):
     qa, sa = orc.quantize(a, 1)
     ws = workspace(dg, M, N, K)
     c = fused(dg, a, qb, sb, ws)
+    assert torch.isfinite(c).all()                  # every element written (NaN prefill)
     g = np.random.default_rng(N)
+    tm, tn = tile_points(M, N, 64, 64, g)
     pm = np.concatenate([g.integers(0, M, 1500), np.full(N, M - 1),
-                         np.arange(M), np.arange(M)])
+                         np.arange(M), np.arange(M), tm])
     pn = np.concatenate([g.integers(0, N, 1500), np.arange(N),
-                         np.zeros(M, dtype=np.int64), np.full(M, N - 1)])
+                         np.zeros(M, dtype=np.int64), np.full(M, N - 1), tn])
     assert pm.max() < M and pn.max() < N
     ref = orc.gemm_nt_points(qa, sa, qb, sb, pm, pn, a_block_rows=1)
     got = c[torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()]

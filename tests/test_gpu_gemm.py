@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import datagen
-from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu, oracle_gemm_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +23,11 @@ def dg():
 
 
 def run_gemm(dg, qa, sa, qb, sb, br, workspace=None):
+    """C starts as NaN everywhere (a fill kernel), so an output element the
+    GEMM never writes cannot pass as a value."""
     M, K = qa.shape
     N = qb.shape[0]
-    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     dg.dg_fp8_gemm_nt(c, dev(qa), dev(qb), dev(sa), dev(sb), br, workspace=workspace)
     torch.cuda.synchronize()
     return c
@@ -49,6 +51,23 @@ def test_gemm_small_full_compare(dg, orc, M, N, K, br):
     ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=br)
     c = bf16_to_f64(run_gemm(dg, qa, sa, qb, sb, br))
     assert_close(c, ref, what="%dx%dx%d/%d" % (M, N, K, br))
+
+
+# Shapes whose tile grid reaches every part of the tile order the full-size
+# launches use: more than 4 rows of 256 x 256 tiles (the 4-row bands swept
+# along N, plus a partial last band), at least 8 tiles (each XCD's
+# contiguous run, tile counts that are not multiples of 8), ragged M and N.
+TILE_ORDER_SHAPES = [(1300, 2312, 256), (2100, 1800, 384), (1040, 4104, 128)]
+
+
+@pytest.mark.parametrize("br", [128, 1])
+@pytest.mark.parametrize("M,N,K", TILE_ORDER_SHAPES)
+def test_gemm_tile_order_full_compare(dg, orc, M, N, K, br):
+    qa, sa, qb, sb = operands(orc, M, N, K, br, seed=M + 3 * N + K)
+    ref = oracle_gemm_rows(orc, qa, sa, qb, sb, br)
+    c = run_gemm(dg, qa, sa, qb, sb, br)
+    assert torch.isfinite(c).all()
+    assert_close(bf16_to_f64(c), ref, what="tile order %dx%dx%d/%d" % (M, N, K, br))
 
 
 def test_gemm_exactness_probe_is_bit_exact(dg, orc):
@@ -100,10 +119,16 @@ def test_gemm_deterministic(dg, orc):
     assert torch.equal(c1, c2)
 
 
-def sample_points(M, N, n_rand=1500, seed=0):
+def sample_points(M, N, n_rand=1500, seed=0, tile=256):
+    """n_rand random points first, then whole rows and columns, then one
+    random point inside every tile x tile block of C."""
     g = np.random.default_rng(seed)
     pm = [g.integers(0, M, n_rand)]
     pn = [g.integers(0, N, n_rand)]
+    tm, tn = np.meshgrid(np.arange(0, M, tile), np.arange(0, N, tile), indexing="ij")
+    tm, tn = tm.ravel(), tn.ravel()
+    pm.append(tm + g.integers(0, tile, tm.size) % np.minimum(tile, M - tm))
+    pn.append(tn + g.integers(0, tile, tn.size) % np.minimum(tile, N - tn))
     for m in sorted({0, M - 1, min(M - 1, M // 2 + 3)}):   # whole rows
         pm.append(np.full(N, m))
         pn.append(np.arange(N))
@@ -119,6 +144,7 @@ def sample_points(M, N, n_rand=1500, seed=0):
 def test_gemm_full_size_sampled(dg, orc, M, N, K, br):
     qa, sa, qb, sb = operands(orc, M, N, K, br, seed=0)
     c = run_gemm(dg, qa, sa, qb, sb, br)
+    assert torch.isfinite(c).all()          # every element written (NaN prefill)
     pm, pn = sample_points(M, N, seed=M + N)
     ref = orc.gemm_nt_points(qa, sa, qb, sb, pm, pn, a_block_rows=br)
     got = c[torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()]
@@ -126,7 +152,6 @@ def test_gemm_full_size_sampled(dg, orc, M, N, K, br):
     # rms of the full output estimated from the random points
     rms = float(np.sqrt(np.mean(ref[:1500] ** 2)))
     assert_close(got, ref, rms=rms, what="%dx%dx%d/%d" % (M, N, K, br))
-    assert torch.isfinite(c.float()).all()
 
 
 @pytest.mark.parametrize("M", [1, 16, 64])
@@ -134,13 +159,14 @@ def test_gemm_full_size_sampled(dg, orc, M, N, K, br):
 def test_gemm_decode_shapes_sampled(dg, orc, M, N, K):
     qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=M)
     ws_bytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda") if ws_bytes else None
     c = run_gemm(dg, qa, sa, qb, sb, 1, workspace=ws)
     c_nows = run_gemm(dg, qa, sa, qb, sb, 1, workspace=None)
-    pm, pn = sample_points(M, N, seed=N)
+    pm, pn = sample_points(M, N, seed=N, tile=64)
     ref = orc.gemm_nt_points(qa, sa, qb, sb, pm, pn, a_block_rows=1)
     rms = float(np.sqrt(np.mean(ref[:1500] ** 2)))
     for cc in (c, c_nows):
+        assert torch.isfinite(cc).all()
         got = cc[torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()]
         assert_close(got.float().cpu().numpy().astype(np.float64), ref, rms=rms,
                      what="decode %dx%dx%d" % (M, N, K))
@@ -173,7 +199,7 @@ def test_gemm_small_m_full_compare(dg, orc, M, N, K, use_ws):
     ws = None
     if use_ws:
         nbytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=1)
     c = bf16_to_f64(run_gemm(dg, qa, sa, qb, sb, 1, workspace=ws))
     assert_close(c, ref, what="small-M %dx%dx%d ws=%s" % (M, N, K, use_ws))
@@ -186,11 +212,49 @@ def test_gemm_small_m_split_k_deterministic_and_repeatable(dg, orc):
     qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=77)
     nbytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
     assert nbytes > 0
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     outs = [run_gemm(dg, qa, sa, qb, sb, 1, workspace=ws) for _ in range(3)]
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
     ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=1)
     assert_close(bf16_to_f64(outs[0]), ref, what="split-K repeat")
+
+
+def test_split_k_calls_on_two_streams_with_distinct_workspaces(dg, orc):
+    """Calls are re-entrant: two split-K GEMMs (different shapes and split
+    counts) launched again and again on two streams of one GPU, each with
+    its own workspace, match the oracle and their single-stream results bit
+    for bit on every round."""
+    shapes = [(16, 4096, 4096), (64, 7168, 2048)]
+    ops, refs, wss, eager = [], [], [], []
+    for i, (M, N, K) in enumerate(shapes):
+        qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=91 + i)
+        ops.append((dev(qa), dev(sa), dev(qb), dev(sb)))
+        refs.append(orc.gemm_nt(qa, sa, qb, sb, a_block_rows=1))
+        nb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+        assert nb > dg.WORKSPACE_COUNTER_BYTES          # both plans split K
+        wss.append(dg.alloc_workspace(nb))
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        a, sa_d, b, sb_d = ops[-1]
+        dg.dg_fp8_gemm_nt(c, a, b, sa_d, sb_d, 1, workspace=wss[-1])
+        torch.cuda.synchronize()
+        eager.append(c)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rnd in range(4):
+        outs = []
+        for i, (M, N, K) in enumerate(shapes):
+            outs.append([torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+                         for _ in range(3)])
+        torch.cuda.synchronize()
+        for j in range(3):                              # interleave the launches
+            for i, st in enumerate(streams):
+                a, sa_d, b, sb_d = ops[i]
+                with torch.cuda.stream(st):
+                    dg.dg_fp8_gemm_nt(outs[i][j], a, b, sa_d, sb_d, 1, workspace=wss[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            for o in outs[i]:
+                assert torch.equal(o.view(torch.int16), eager[i].view(torch.int16)), rnd
+            assert_close(bf16_to_f64(outs[i][0]), refs[i], what="two streams %d" % i)
 
 
 def test_outlier_activations_block_vs_global_full_size(dg, orc):
@@ -249,7 +313,7 @@ def test_graph_replays_match_eager(dg, orc, M, N, K, br):
     qa, sa, qb, sb = operands(orc, M, N, K, br, seed=K + M)
     a, b, sa_d, sb_d = dev(qa), dev(qb), dev(sa), dev(sb)
     wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
     c_eager = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     dg.dg_fp8_gemm_nt(c_eager, a, b, sa_d, sb_d, br, workspace=ws)
     torch.cuda.synchronize()
@@ -290,10 +354,12 @@ def check_at_limit(dg, orc, M, N, K, br):
     sa = (torch.rand((K // 128, (M + br - 1) // br), device="cuda", generator=g) + 0.5) * 1e-3
     sb = (torch.rand((K // 128, (N + 127) // 128), device="cuda", generator=g) + 0.5) * 1e-3
     wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
-    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     dg.dg_fp8_gemm_nt(c, qa, qb, sa, sb, br, workspace=ws)
     torch.cuda.synchronize()
+    assert torch.isfinite(c).all()
+    tile_points_at_limit(orc, qa, sa, qb, sb, c, br)
     rows = np.array(sorted({0, min(1, M - 1), min(255, M - 1), min(256, M - 1), M // 2, max(M - 2, 0),
                             M - 1}), np.int64)
     assert rows.max() < M
@@ -318,6 +384,33 @@ def check_at_limit(dg, orc, M, N, K, br):
     assert_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="limit %dx%dx%d" % (M, N, K))
     del qa, qb, c
     torch.cuda.empty_cache()
+
+
+def tile_points_at_limit(orc, qa, sa, qb, sb, c, br, tile=256):
+    """One point in every tile x tile block of C: rows r_i (one per row band)
+    crossed with columns n_j (one per column band), the reference computed
+    one column at a time with that column's B row alone in a 128-row block
+    (so the oracle reads its own column's block scales)."""
+    M, K = qa.shape
+    N = qb.shape[0]
+    g = np.random.default_rng(M + N)
+    rows = np.array([r + g.integers(0, min(tile, M - r)) for r in range(0, M, tile)], np.int64)
+    cols = np.array([n + g.integers(0, min(tile, N - n)) for n in range(0, N, tile)], np.int64)
+    qa_h = qa[torch.from_numpy(rows).cuda()].cpu().numpy()
+    sa_h = np.ascontiguousarray(sa[:, torch.from_numpy(rows // br).cuda()].cpu().numpy())
+    qb_h = qb[torch.from_numpy(cols).cuda()].cpu().numpy()
+    sb_h = sb[:, torch.from_numpy(cols // 128).cuda()].cpu().numpy()
+    got = c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    got = got.float().cpu().numpy().astype(np.float64)
+    ref = np.empty((rows.size, cols.size))
+    blk = np.zeros((128, K), np.uint8)
+    pm = np.arange(rows.size)
+    for j in range(cols.size):
+        blk[0] = qb_h[j]
+        ref[:, j] = orc.gemm_nt_points(qa_h, sa_h, blk, np.ascontiguousarray(sb_h[:, j:j + 1]),
+                                       pm, np.zeros_like(pm), a_block_rows=1)
+    assert_close(got, ref, rms=float(np.sqrt(np.mean(ref ** 2))),
+                 what="limit tiles %dx%dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M,N,K,br", [

@@ -83,7 +83,7 @@ def test_graph_fused_activation_quantisation(dg, orc, M, N, K):
     a = dev(datagen.normal((M, K), 1.0, seed=3, stream=0))
     _, _, qb, sb = quantised(orc, 1, N, K)
     wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
     check_graph(bf16(M, N), lambda o: dg.dg_fp8_gemm_nt_fused_a(o[0], a, qb, sb, workspace=ws))
 
 
@@ -94,7 +94,7 @@ def test_graph_epilogue_with_residual(dg, orc, M, N, K, act):
     n_out = N // 2 if act == "swiglu" else N
     r = dev(datagen.normal((M, n_out), 1.0, seed=5)).to(torch.bfloat16)
     wsb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device="cuda")
     check_graph(bf16(M, n_out), lambda o: dg.dg_fp8_gemm_nt_epilogue(
         o[0], qa, qb, sa, sb, 1, act=act, residual=r, workspace=ws))
 
@@ -116,7 +116,7 @@ def test_graph_layouts(dg, orc, layout):
     a = dev(np.ascontiguousarray(qa.T) if layout in ("tn", "tt") else qa)
     b = dev(np.ascontiguousarray(qb.T) if layout in ("tn", "nn") else qb)
     sa_d, sb_d = dev(sa), dev(sb)
-    ws = torch.empty(dg.dg_fp8_gemm_workspace_bytes(M, N, K, layout), dtype=torch.uint8,
+    ws = torch.zeros(dg.dg_fp8_gemm_workspace_bytes(M, N, K, layout), dtype=torch.uint8,
                      device="cuda")
     check_graph(bf16(M, N), lambda o: dg.dg_fp8_gemm(o[0], a, b, sa_d, sb_d, 1, layout=layout,
                                                      workspace=ws))
@@ -142,7 +142,7 @@ def test_graph_masked_grouped(dg, orc):
     mm = dev(np.array([16, 0, 5, 16, 9, 1, 12, 3], np.int32))
     n = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, max_m, N, K)
     assert n > 0                                  # the split-K plan (counters across replays)
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     A, B, SA, SB = dev(qa), dev(qb), dev(sa), dev(sb)
     check_graph(lambda: [torch.zeros((G, max_m, N), dtype=torch.bfloat16, device="cuda")],
                 lambda o: dg.dg_fp8_grouped_gemm_masked(o[0], A, B, SA, SB, 1, mm, workspace=ws))

@@ -88,9 +88,14 @@ def test_grouped_single_expert_equals_dense(dg, orc):
     assert np.array_equal(c[mi >= 0], bf16_to_f64(cd)[mi >= 0])
 
 
+@pytest.mark.parametrize("br", [1, 128])
 @pytest.mark.parametrize("proj,N,K", [("up", 11008, 4096), ("down", 4096, 11008)])
-def test_grouped_moe_full_size_sampled(dg, orc, proj, N, K):
-    """8 experts, 1024 tokens routed top-2, rows padded to 128 per expert."""
+def test_grouped_moe_full_size_sampled(dg, orc, proj, N, K, br):
+    """8 experts, 1024 tokens routed top-2, rows padded to 128 per expert;
+    activations with 1x128 scales (tokens quantised per row before routing)
+    and with 128x128 scales (valid too: no block spans two experts).  C
+    starts as NaN; every element must be written; sampled points include one
+    in every 128-row x 256-column tile that holds real rows."""
     G, tokens = 8, 1024
     r = datagen.moe_routing(tokens, G, 2, align=128, seed=0)
     mi = r["m_indices"]
@@ -101,24 +106,32 @@ def test_grouped_moe_full_size_sampled(dg, orc, proj, N, K):
     else:
         a = datagen.normal((M, K), 1.0, seed=0, stream=3)
         a[mi < 0] = 0.0
-    qa, sa = orc.quantize(a, 1)
+    qa, sa = orc.quantize(a, br)
     w = datagen.normal((G * N, K), 0.02, seed=0, stream=2)
     qb = np.empty((G, N, K), np.uint8)
     sb = np.empty((G, K // 128, N // 128), np.float32)
     for e in range(G):
         qb[e], sb[e] = orc.quantize(w[e * N:(e + 1) * N], 128)
-    c = run(dg, qa, sa, qb, sb, mi, 1)
+    c = run(dg, qa, sa, qb, sb, mi, br)
+    assert np.all(np.isfinite(c))
     assert np.all(c[mi < 0] == 0.0)
     g = np.random.default_rng(1)
     real_rows = np.nonzero(mi >= 0)[0]
-    pm = g.choice(real_rows, 2000)
-    pn = g.integers(0, N, 2000)
-    ref = np.empty(2000)
+    pm = [g.choice(real_rows, 2000)]
+    pn = [g.integers(0, N, 2000)]
+    for blk in range(M // 128):                      # one point per tile with real rows
+        rr = real_rows[(real_rows >= blk * 128) & (real_rows < blk * 128 + 128)]
+        if rr.size:
+            n0 = np.arange(0, N, 256)
+            pm.append(g.choice(rr, n0.size))
+            pn.append(n0 + g.integers(0, 256, n0.size) % np.minimum(256, N - n0))
+    pm, pn = np.concatenate(pm), np.concatenate(pn)
+    ref = np.empty(pm.size)
     for e in range(G):
         sel = mi[pm] == e
         if sel.any():
             # rows of one expert: the dense oracle on that expert's weights
-            ref[sel] = orc.gemm_nt_points(qa, sa, qb[e], sb[e], pm[sel], pn[sel], a_block_rows=1)
+            ref[sel] = orc.gemm_nt_points(qa, sa, qb[e], sb[e], pm[sel], pn[sel], a_block_rows=br)
     assert_close(c[pm, pn], ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="moe " + proj)
 
 

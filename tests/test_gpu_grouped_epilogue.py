@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import datagen
-from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu, tile_points
 
 pytestmark = pytest.mark.gpu
 
@@ -105,11 +105,13 @@ def test_grouped_swiglu_moe_shape_sampled(dg, orc):
     dg.dg_fp8_grouped_gemm_contig(c, dev(qa), dev(qb), dev(sa), dev(sb), 1, dev(mi), act="swiglu")
     torch.cuda.synchronize()
     got = bf16_to_f64(c)
+    assert np.all(np.isfinite(got))                 # every element written (NaN prefill)
     assert np.all(got[mi < 0] == 0.0)
     rng = np.random.default_rng(5)
-    pm = rng.choice(np.nonzero(mi >= 0)[0], 3000)
-    pj = rng.integers(0, N // 2, 3000)
-    acc = np.empty((3000, 2))
+    tm, tj = tile_points(M, N // 2, 128, 128, rng, rows=np.nonzero(mi >= 0)[0])
+    pm = np.concatenate([rng.choice(np.nonzero(mi >= 0)[0], 3000), tm])
+    pj = np.concatenate([rng.integers(0, N // 2, 3000), tj])
+    acc = np.empty((pm.size, 2))
     for e in range(G):
         sel = mi[pm] == e
         for h in range(2):   # gate (column 2j) and up (2j + 1)
@@ -147,7 +149,7 @@ def test_masked_epilogue(dg, orc, act, residual, ws):
     if ws:
         nb = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, max_m, N, K)
         assert nb > 0
-        w = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        w = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     dg.dg_fp8_grouped_gemm_masked(c, dev(qa), dev(qb), dev(sa), dev(sb), 1, dev(mm), workspace=w,
                                   act=act, residual=res)
     torch.cuda.synchronize()

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import datagen
-from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu, tile_points
 
 pytestmark = pytest.mark.gpu
 
@@ -52,11 +52,11 @@ def test_gemm_layouts(dg, orc, layout, M, N, K, br):
     a = np.ascontiguousarray(qa.T) if layout in ("tn", "tt") else qa
     b = np.ascontiguousarray(qb.T) if layout in ("tn", "nn") else qb
     nb = dg.dg_fp8_gemm_workspace_bytes(M, N, K, layout)
-    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     dg.dg_fp8_gemm(c, dev(a), dev(b), dev(sa), dev(sb), br, layout=layout, workspace=ws)
     nt_ws = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-    w2 = torch.empty(max(nt_ws, 16), dtype=torch.uint8, device="cuda") if nt_ws else None
+    w2 = torch.zeros(max(nt_ws, 16), dtype=torch.uint8, device="cuda") if nt_ws else None
     c_nt = torch.empty_like(c)
     dg.dg_fp8_gemm_nt(c_nt, dev(qa), dev(qb), dev(sa), dev(sb), br, workspace=w2)
     torch.cuda.synchronize()
@@ -64,6 +64,37 @@ def test_gemm_layouts(dg, orc, layout, M, N, K, br):
     if M * N * K <= (1 << 31):
         ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=br)
         assert_close(bf16_to_f64(c), ref, what="%s %dx%dx%d" % (layout, M, N, K))
+
+
+@pytest.mark.parametrize("extra", ["copies_only", "full"])
+def test_gemm_layout_workspace_between_copies_and_split_k(dg, orc, extra):
+    """M = 16, N = K = 4096 in the NN layout (B transposed into the
+    workspace): with room for the counter region and the copy only (plus 16
+    bytes, less than the split-K partials) the call runs without split-K;
+    with the full size it splits K.  Both succeed, give the two-call result,
+    and leave the counter region zero, so the same workspace then serves a
+    split-K dg_fp8_gemm_nt call."""
+    M, N, K = 16, 4096, 4096
+    qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=23)
+    b_nn = np.ascontiguousarray(qb.T)
+    full = dg.dg_fp8_gemm_workspace_bytes(M, N, K, "nn")
+    nt = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+    assert nt > dg.WORKSPACE_COUNTER_BYTES and full == nt + N * K
+    nb = dg.WORKSPACE_COUNTER_BYTES + N * K + 16 if extra == "copies_only" else full
+    ws = torch.zeros(max(nb, nt), dtype=torch.uint8, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm(c, dev(qa), dev(b_nn), dev(sa), dev(sb), 1, layout="nn", workspace=ws[:nb])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:dg.WORKSPACE_COUNTER_BYTES]) == 0
+    ref = orc.gemm_nt(qa, sa, qb, sb, a_block_rows=1)
+    assert_close(bf16_to_f64(c), ref, what="nn workspace " + extra)
+    c2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dg.dg_fp8_gemm_nt(c2, dev(qa), dev(qb), dev(sa), dev(sb), 1, workspace=ws[:nt])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:dg.WORKSPACE_COUNTER_BYTES]) == 0
+    assert_close(bf16_to_f64(c2), ref, what="nt after nn")
+    if extra == "full":                             # same plan: identical bits
+        assert torch.equal(c.view(torch.int16), c2.view(torch.int16))
 
 
 def test_gemm_layout_needs_its_workspace(dg, orc):
@@ -115,11 +146,13 @@ def test_k_grouped_weight_gradient_shape_sampled(dg, orc):
     K = ko[-1]
     qa, sa, qb, sb = operands(orc, M, N, K, 1, seed=11)
     c = run_k_grouped(dg, qa, sa, qb, sb, 1, ko)
+    assert torch.isfinite(c).all()                  # every element written (NaN prefill)
     g_rng = np.random.default_rng(5)
     for g in range(len(sizes)):
         k0, k1 = ko[g], ko[g + 1]
-        pm = np.concatenate([g_rng.integers(0, M, 600), np.full(64, M - 1)])
-        pn = np.concatenate([g_rng.integers(0, N, 600), np.arange(0, N, N // 64)])
+        tm, tn = tile_points(M, N, 256, 256, g_rng)
+        pm = np.concatenate([g_rng.integers(0, M, 600), np.full(64, M - 1), tm])
+        pn = np.concatenate([g_rng.integers(0, N, 600), np.arange(0, N, N // 64), tn])
         assert pm.max() < M and pn.max() < N
         ref = orc.gemm_nt_points(np.ascontiguousarray(qa[:, k0:k1]),
                                  np.ascontiguousarray(sa[k0 // 128:k1 // 128]),

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import datagen
-from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu, tile_points
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def run(dg, qa, sa, qb, sb, mm, br, workspace):
     ws = None
     if workspace:
         n = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, max_m, N, qa.shape[2])
-        ws = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(n, 16), dtype=torch.uint8, device="cuda")
     dg.dg_fp8_grouped_gemm_masked(c, dev(qa), dev(qb), dev(sa), dev(sb), br,
                                   dev(np.asarray(mm, np.int32)), workspace=ws)
     torch.cuda.synchronize()
@@ -66,6 +66,7 @@ CASES = [
     (2, 100, 256, 256, 1, [100, 70]),        # two 64-row chunks per group
     (8, 1, 4096, 2048, 1, [1, 0, 1, 1, 0, 1, 1, 1]),
     (5, 32, 136, 1280, 128, [-5, 40, 32, 31, 0]),  # out-of-range masks count as clamped
+    (2, 200, 512, 512, 128, [200, 150]),     # four chunks, rows past 128: second A scale block
 ]
 
 
@@ -130,7 +131,13 @@ def test_masked_decode_moe_full_size_sampled(dg, orc, N, K):
     pg = rng.integers(0, G, 2000)
     pm = (rng.random(2000) * mm[pg]).astype(np.int64)
     pn = rng.integers(0, N, 2000)
-    ref = np.empty(2000)
+    for g in range(G):                              # one point per group and 128-column tile
+        if mm[g] > 0:
+            tm, tn = tile_points(int(mm[g]), N, 64, 128, rng)
+            pg = np.concatenate([pg, np.full(tm.size, g)])
+            pm = np.concatenate([pm, tm])
+            pn = np.concatenate([pn, tn])
+    ref = np.empty(pm.size)
     for g in range(G):
         sel = pg == g
         ref[sel] = orc.gemm_nt_points(qa[g], sa[g], qb[g], sb[g], pm[sel], pn[sel], a_block_rows=1)

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import datagen
-from gpu_util import assert_close, bf16_to_f64, dev, need_gpu
+from gpu_util import assert_close, bf16_to_f64, dev, need_gpu, oracle_gemm_rows, tile_points
 
 pytestmark = pytest.mark.gpu
 
@@ -76,7 +76,7 @@ def operands(orc, M, N, K, br, seed=0):
 
 def run_gemm(dg, orc, qa, ea, qb, eb, br):
     M, N = qa.shape[0], qb.shape[0]
-    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    c = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
     dg.dg_fp8_gemm_nt_ue8m0(c, dev(qa), dev(qb), dev(orc.pack_ue8m0(ea)),
                             dev(orc.pack_ue8m0(eb)), br)
     torch.cuda.synchronize()
@@ -86,11 +86,14 @@ def run_gemm(dg, orc, qa, ea, qb, eb, br):
 @pytest.mark.parametrize("br", [128, 1])
 @pytest.mark.parametrize("M,N,K", [(128, 256, 512), (256, 256, 128), (512, 768, 384),
                                    (300, 520, 1024), (200, 264, 640), (1, 256, 256),
-                                   (16, 512, 1664), (257, 136, 128)])
+                                   (16, 512, 1664), (257, 136, 128),
+                                   # tile order of the full-size launches: > 4 tile rows,
+                                   # >= 8 tiles, ragged
+                                   (1300, 2312, 256), (2100, 1800, 384)])
 def test_gemm_ue8m0_small_full_compare(dg, orc, M, N, K, br):
     """Several tiles, ragged M and N, K-block counts that leave partial words."""
     qa, ea, qb, eb = operands(orc, M, N, K, br, seed=M + N + K)
-    ref = orc.gemm_nt(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), a_block_rows=br)
+    ref = oracle_gemm_rows(orc, qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), br)
     c = bf16_to_f64(run_gemm(dg, orc, qa, ea, qb, eb, br))
     assert_close(c, ref, what="ue8m0 %dx%dx%d/%d" % (M, N, K, br))
 
@@ -134,9 +137,11 @@ def test_gemm_ue8m0_full_size_sampled(dg, orc):
     M, N, K, br = 4096, 4096, 7168, 128
     qa, ea, qb, eb = operands(orc, M, N, K, br)
     c = run_gemm(dg, orc, qa, ea, qb, eb, br)
+    assert torch.isfinite(c).all()                  # every element written (NaN prefill)
     g = np.random.default_rng(1)
-    pm = np.concatenate([g.integers(0, M, 1500), np.full(N, M - 1), np.arange(0, M, 8)])
-    pn = np.concatenate([g.integers(0, N, 1500), np.arange(N), np.full(M // 8, N - 1)])
+    tm, tn = tile_points(M, N, 256, 256, g)
+    pm = np.concatenate([g.integers(0, M, 1500), np.full(N, M - 1), np.arange(0, M, 8), tm])
+    pn = np.concatenate([g.integers(0, N, 1500), np.arange(N), np.full(M // 8, N - 1), tn])
     assert pm.max() < M and pn.max() < N
     ref = orc.gemm_nt_points(qa, orc.ue8m0_scales(ea), qb, orc.ue8m0_scales(eb), pm, pn,
                              a_block_rows=br)
@@ -179,7 +184,7 @@ def test_gemm_ue8m0_small_m(dg, orc, M, N, K, use_ws):
     ws = None
     if use_ws:
         nb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     dg.dg_fp8_gemm_nt_ue8m0(c, dev(qa), dev(qb), dev(orc.pack_ue8m0(ea)), dev(orc.pack_ue8m0(eb)),
                             1, workspace=ws)
@@ -203,7 +208,7 @@ def test_gemm_ue8m0_small_m_extreme_exponents(dg, orc):
             ws = None
             if use_ws:
                 nb = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
-                ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+                ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
             c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             dg.dg_fp8_gemm_nt_ue8m0(c, dev(qa), dev(qb), dev(orc.pack_ue8m0(ea)),
                                     dev(orc.pack_ue8m0(eb)), 1, workspace=ws)
@@ -262,15 +267,24 @@ def test_grouped_gemm_ue8m0_one_expert_equals_dense(dg, orc):
     assert np.array_equal(bf16_to_f64(c)[real], bf16_to_f64(cd)[real])
 
 
+MASKED_UE8M0_CASES = [
+    # G, max_m, N, K, br, masks
+    (6, 40, 1024, 4224, 1, [40, 0, 9, 33, 1, 17]),
+    (6, 40, 1024, 4224, 128, [40, 0, 9, 33, 1, 17]),
+    (3, 100, 512, 1152, 1, [100, 64, 65]),        # two 64-row chunks: row offset 64
+    (2, 200, 512, 640, 128, [200, 130]),          # four chunks, second 128-row scale block
+]
+
+
 @pytest.mark.parametrize("ws", [False, True])
-@pytest.mark.parametrize("br", [1, 128])
-def test_masked_grouped_gemm_ue8m0(dg, orc, br, ws):
+@pytest.mark.parametrize("G,max_m,N,K,br,mm", MASKED_UE8M0_CASES)
+def test_masked_grouped_gemm_ue8m0(dg, orc, G, max_m, N, K, br, mm, ws):
     """Masked grouped layout with UE8M0 scales: valid rows within the GEMM
     tolerance of the oracle's masked product (exponents as FP32 powers of
-    two), rows past the counts untouched; K-block count leaving partial
-    exponent words; with and without the split-K workspace."""
-    G, max_m, N, K = 6, 40, 1024, 4224
-    mm = np.array([40, 0, 9, 33, 1, 17], np.int32)
+    two), rows past the counts untouched; K-block counts leaving partial
+    exponent words; several row chunks per group (A rows and exponent words
+    offset per chunk); with and without the split-K workspace."""
+    mm = np.array(mm, np.int32)
     qa = np.empty((G, max_m, K), np.uint8)
     qb = np.empty((G, N, K), np.uint8)
     eas, ebs = [], []
@@ -286,7 +300,7 @@ def test_masked_grouped_gemm_ue8m0(dg, orc, br, ws):
     if ws:
         nb = dg.dg_fp8_grouped_gemm_masked_workspace_bytes(G, max_m, N, K)
         assert nb > 0
-        w = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        w = torch.zeros(nb, dtype=torch.uint8, device="cuda")
     dg.dg_fp8_grouped_gemm_masked_ue8m0(c, dev(qa), dev(qb), dev(sfa), dev(sfb), br, dev(mm),
                                         workspace=w)
     torch.cuda.synchronize()
