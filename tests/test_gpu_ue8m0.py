@@ -271,8 +271,8 @@ MASKED_UE8M0_CASES = [
     # G, max_m, N, K, br, masks
     (6, 40, 1024, 4224, 1, [40, 0, 9, 33, 1, 17]),
     (6, 40, 1024, 4224, 128, [40, 0, 9, 33, 1, 17]),
-    (3, 100, 512, 1152, 1, [100, 64, 65]),        # two 64-row chunks: row offset 64
-    (2, 200, 512, 640, 128, [200, 130]),          # four chunks, second 128-row scale block
+    (3, 100, 256, 4224, 1, [100, 64, 65]),        # two 64-row chunks: row offset 64
+    (2, 200, 256, 4224, 128, [200, 130]),         # four chunks, second 128-row scale block
 ]
 
 
