@@ -94,6 +94,8 @@ def _load():
     lib.dg_fp8_grouped_gemm_masked.restype = i32
     lib.dg_fp8_grouped_gemm_masked.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp,
                                                ctypes.c_size_t, vp]
+    lib.dg_fp8_gemm_nt_noalloc.restype = i32
+    lib.dg_fp8_gemm_nt_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     if lib.dg_abi_version() != ABI_VERSION:
         raise ImportError("libdg ABI %d != binding ABI %d" % (lib.dg_abi_version(), ABI_VERSION))
     return lib
@@ -213,6 +215,32 @@ def dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows: int = 128, workspace=None,
     _check(lib.dg_fp8_gemm_nt(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), a_block_rows,
                               M, N, K, _ptr(workspace), ws_bytes, _stream(stream)),
            "dg_fp8_gemm_nt")
+
+
+# static split-K scratch of dg_fp8_gemm_nt_noalloc, per GPU (dg.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def dg_fp8_gemm_nt_noalloc(c, a, b, sa, sb, a_block_rows: int = 128, stream=None) -> None:
+    """dg_fp8_gemm_nt without a workspace argument, for callers that cannot
+    allocate: the split-K scratch is the library's static per-GPU array
+    (calls that overlap on one GPU race on it)."""
+    c = _bf16(c, "c")
+    a = _codes(a, "a")
+    b = _codes(b, "b")
+    _require(sa, torch.float32, "sa")
+    _require(sb, torch.float32, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or c.shape != (M, N):
+        raise ValueError("shape mismatch: a %s, b %s, c %s" % (tuple(a.shape), tuple(b.shape),
+                                                              tuple(c.shape)))
+    if sa.numel() != cdiv(K, 128) * cdiv(M, a_block_rows):
+        raise ValueError("sa must hold (K/128)*ceil(M/a_block_rows) floats")
+    if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
+        raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
+    _check(lib.dg_fp8_gemm_nt_noalloc(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb), a_block_rows,
+                                      M, N, K, _stream(stream)), "dg_fp8_gemm_nt_noalloc")
 
 
 def dg_quantize_fp8_block_ue8m0(q, sf, x, block_rows: int = 128, stream=None) -> None:
@@ -551,7 +579,7 @@ __all__ = [
     "dg_fp8_gemm", "LAYOUTS", "dg_fp8_grouped_gemm_k", "fp8_gemm_nt", "fp8_grouped_gemm_contig",
     "dg_fp8_grouped_gemm_masked", "dg_fp8_grouped_gemm_masked_workspace_bytes",
     "dg_fp8_grouped_gemm_contig_ue8m0", "dg_fp8_grouped_gemm_masked_ue8m0", "alloc_workspace",
-    "WORKSPACE_COUNTER_BYTES",
+    "WORKSPACE_COUNTER_BYTES", "dg_fp8_gemm_nt_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 # (the _epilogue C entry points are reached through the act / residual
 # arguments of dg_fp8_grouped_gemm_contig and dg_fp8_grouped_gemm_masked)

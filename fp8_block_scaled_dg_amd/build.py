@@ -18,7 +18,7 @@ LIBDIR = os.path.join(PKG, "lib")
 OBJDIR = os.path.join(LIBDIR, "obj")
 LIB = os.path.join(LIBDIR, "libdg.so")
 SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "gemm_stream.hip", "transpose.hip",
-           "api.cpp"]
+           "noalloc.hip", "api.cpp"]
 # measurement probe (its own library; not part of the C ABI in include/dg.h)
 PROBE_LIB = os.path.join(LIBDIR, "libdg_probe.so")
 PROBE_SOURCES = ["probe/peak.hip"]

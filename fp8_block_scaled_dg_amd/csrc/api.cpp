@@ -73,6 +73,7 @@ const char* dg_status_string(int status) {
     case DG_ERR_ALIGN: return "pointer not suitably aligned";
     case DG_ERR_WORKSPACE: return "workspace smaller than required";
     case DG_ERR_HIP: return "HIP runtime error";
+    case DG_ERR_SCRATCH: return "shape needs more split-K scratch than the static array holds";
     default: return "unknown status";
   }
 }
@@ -382,6 +383,32 @@ int dg_fp8_grouped_gemm_masked_epilogue(uint16_t* c, const uint8_t* a, const uin
   p.epi.res = residual;
   return from_hip(dg::launch_gemm_skinny_masked(p, masked_m, max_m, workspace, workspace_bytes,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+int dg_fp8_gemm_nt_noalloc(uint16_t* c, const uint8_t* a, const uint8_t* b, const float* sa,
+                           const float* sb, int a_block_rows, int64_t M, int64_t N, int64_t K,
+                           void* stream) {
+  const int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
+  if (st != DG_OK) return st;
+  // plans that split K: the LDS-ring small-M kernel with a non-zero workspace
+  const bool split = dg::skinny_applies(M, N, K) && !dg::stream_preferred(M, N, K) &&
+                     dg::skinny_workspace_bytes(M, N, K) > 0;
+  if (!split) return dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, M, N, K, nullptr, 0, stream);
+  const size_t need = dg::skinny_workspace_bytes(M, N, K);
+  if (need > DG_NOALLOC_SCRATCH_BYTES) return DG_ERR_SCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return DG_ERR_HIP;
+  if (s) {  // the scratch address is the current device's
+    int sdev = 0;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return DG_ERR_HIP;
+    if (sdev != cur) return DG_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  if (dg::noalloc_scratch(&ws) != hipSuccess) return DG_ERR_HIP;
+  const int zs = from_hip(dg::launch_zero_counters(ws, s));
+  if (zs != DG_OK) return zs;
+  return dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, M, N, K, ws, need, stream);
 }
 
 }  // extern "C"

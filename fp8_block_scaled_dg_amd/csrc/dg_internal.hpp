@@ -90,6 +90,12 @@ int64_t skinny_masked_grid(int num_groups, int64_t max_m, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny_masked(const GemmProblem& p, const int32_t* masked_m, int64_t max_m,
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+// Static scratch of dg_fp8_gemm_nt_noalloc: its device address on the
+// current device (looked up once per device), and a kernel that zeroes its
+// counter region.
+hipError_t noalloc_scratch(void** ptr);
+hipError_t launch_zero_counters(void* scratch_ptr, hipStream_t stream);
+
 // Streaming small-M kernel (no workspace), and whether it is the better of
 // the two small-M kernels for a shape.
 hipError_t launch_gemm_stream(const GemmProblem& p, hipStream_t stream);

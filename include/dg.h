@@ -58,7 +58,8 @@ enum {
     DG_ERR_UNSUPPORTED = 3, /* block_rows / group count / epilogue unknown  */
     DG_ERR_ALIGN = 4,       /* a pointer is not suitably aligned            */
     DG_ERR_WORKSPACE = 5,   /* workspace given but smaller than required    */
-    DG_ERR_HIP = 6          /* the HIP runtime reported an error            */
+    DG_ERR_HIP = 6,         /* the HIP runtime reported an error            */
+    DG_ERR_SCRATCH = 7      /* shape needs more than the static scratch     */
 };
 
 /* ABI version of the loaded library (compare with DG_ABI_VERSION). */
@@ -376,6 +377,35 @@ int dg_fp8_grouped_gemm_masked_ue8m0(uint16_t *c, const uint8_t *a, const uint8_
                                      const int32_t *masked_m, int num_groups, int64_t max_m,
                                      int64_t N, int64_t K, void *workspace,
                                      size_t workspace_bytes, void *stream);
+
+/*
+ * dg_fp8_gemm_nt for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same operation, arguments (minus the workspace), requirements, kernel plan
+ * and results, bit for bit, as dg_fp8_gemm_nt given a workspace of
+ * dg_fp8_gemm_nt_workspace_bytes(M, N, K).  The split-K scratch (arrival
+ * counters and partial tiles) is a static device array inside the library
+ * instead: DG_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held
+ * until the process ends.
+ *   - Runs on the current device; a non-NULL stream must belong to it
+ *     (DG_ERR_UNSUPPORTED otherwise).
+ *   - A shape whose plan needs more than DG_NOALLOC_SCRATCH_BYTES of scratch
+ *     gives DG_ERR_SCRATCH with nothing enqueued (the small-M plans need at
+ *     most 8 MiB plus DG_WORKSPACE_COUNTER_BYTES, so none does today).
+ *   - A call whose plan splits K first clears the counter region with a fill
+ *     kernel on `stream`, then runs the GEMM; plans without split-K touch
+ *     no scratch.
+ *   - Every call on one GPU shares that GPU's array and leaves its contents
+ *     behind: calls that may overlap on one GPU (different streams) race on
+ *     it and must be ordered by the caller.
+ *   - The first call on a device looks the array's device address up
+ *     (hipGetSymbolAddress, with that device current) and keeps it.  No call
+ *     allocates or frees memory.
+ */
+#define DG_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dg_fp8_gemm_nt_noalloc(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                           const float *sa, const float *sb, int a_block_rows,
+                           int64_t M, int64_t N, int64_t K, void *stream);
 
 #ifdef __cplusplus
 }

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(dg):
 
 def test_abi_version_and_status_strings(dg):
     assert dg.lib.dg_abi_version() == 2 == dg.ABI_VERSION
-    for st in range(0, 7):
+    for st in range(0, 8):
         assert dg.status_string(st) and dg.status_string(st) != "unknown status"
     assert dg.status_string(99) == "unknown status"
     assert dg.get_mk_alignment_for_contiguous_layout() == 128
@@ -249,3 +249,21 @@ def test_grouped_ue8m0_validation(dg):
     assert gu(mi=None) == 1 and gu(G=0) == 3 and gu(br=7) == 3
     assert gu(M=200) == 2 and gu(K=100) == 2
     assert gu(mi=ctypes.c_void_p(0x10002)) == 4
+
+
+def test_noalloc_validation(dg):
+    """The no-allocation GEMM validates like dg_fp8_gemm_nt before any HIP
+    call."""
+    lib = dg.lib
+
+    def gn(c=P, a=P, b=P, sa=P, sb=P, br=1, M=64, N=4096, K=4096):
+        return lib.dg_fp8_gemm_nt_noalloc(c, a, b, sa, sb, br, M, N, K, None)
+    for kw in ("c", "a", "b", "sa", "sb"):
+        assert gn(**{kw: None}) == 1
+    assert gn(br=2) == 3
+    assert gn(M=0) == 2 and gn(N=260) == 2 and gn(K=200) == 2
+    assert gn(a=P1) == 4
+    # every small-M plan fits the static scratch
+    for M in (1, 5, 16, 17, 33, 64):
+        for N in (8, 1000, 4096, 7168, 8192, 16384, 24576, 65536):
+            assert dg.dg_fp8_gemm_nt_workspace_bytes(M, N, 16384) <= dg.NOALLOC_SCRATCH_BYTES
