@@ -8,6 +8,7 @@ exact-rational nearest search (tests/exact.py), and the oracle's second
 encoder, a brute-force table search written separately from the arithmetic
 encoder.
 """
+import concurrent.futures as cf
 import json
 import os
 from fractions import Fraction
@@ -134,16 +135,40 @@ def test_exact_rational_nearest_on_sample(orc):
 
 
 @pytest.mark.slow
-def test_arith_encoder_matches_torch_on_strided_sweep_of_all_binary32(orc):
-    """Every 13th binary32 bit pattern with |v| <= 464, both signs: the
-    arithmetic encoder equals PyTorch's float8_e4m3fn cast (which rounds to
-    nearest-even and agrees with saturation up to 464)."""
+def test_arith_encoder_matches_torch_on_every_binary32(orc):
+    """Every binary32 bit pattern with |v| <= 464, both signs (2.3e9 values):
+    the arithmetic encoder equals PyTorch's float8_e4m3fn cast (which rounds
+    to nearest-even and agrees with saturation up to 464).  Chunks of 2^24
+    patterns run on host threads (the oracle's C code releases the GIL)."""
     top = 0x43E80000  # 464.0
-    for start in range(0, top + 1, 1 << 26):
-        bits = np.arange(start, min(start + (1 << 26), top + 1), 13, dtype=np.uint32)
+    starts = list(range(0, top + 1, 1 << 24))
+
+    def chunk(start):
+        bits = np.arange(start, min(start + (1 << 24), top + 1), dtype=np.uint32)
         v = bits.view(np.float32)
-        assert np.array_equal(orc.e4m3_encode(v), _torch_cast(v))
-        assert np.array_equal(orc.e4m3_encode(-v), _torch_cast(-v))
+        for w in (v, -v):
+            if not np.array_equal(orc.e4m3_encode(w), _torch_cast(w)):
+                return start
+        return None
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        bad = [s for s in ex.map(chunk, starts) if s is not None]
+    assert not bad, [hex(b) for b in bad[:4]]
+
+
+def test_search_encoder_near_every_code_and_midpoint(orc):
+    """The brute-force search encoder against the arithmetic one on every
+    binary32 within 64 ulps of each E4M3 value and each rounding midpoint
+    (both signs), and on every 4096th pattern below 464."""
+    vals = orc.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    pts = np.concatenate([vals, mids, [448.0, 456.0, 464.0]]).astype(np.float32)
+    u = pts.view(np.uint32).astype(np.int64)
+    near = (u[:, None] + np.arange(-64, 65)[None, :]).ravel()
+    near = near[(near >= 0) & (near <= 0x43E80000)].astype(np.uint32)
+    sweep = np.arange(0, 0x43E80001, 4096, dtype=np.uint32)
+    v = np.concatenate([near, sweep]).view(np.float32)
+    v = np.concatenate([v, -v])
+    assert np.array_equal(orc.e4m3_encode(v, "search"), orc.e4m3_encode(v, "arith"))
 
 
 def test_two_step_rounding_vectors(orc):
