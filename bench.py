@@ -302,6 +302,7 @@ class Dense:
         oracle.e4m3_decode(np.zeros(1, np.uint8))      # load the library before threading
         total = 0.0
         spent = 0.0
+        quant_s = gemm_s = 0.0
         with cf.ThreadPoolExecutor(max_workers=threads) as ex:
             for it in self.items:
                 M, N, K = it["M"], it["N"], it["K"]
@@ -329,15 +330,56 @@ class Dense:
                 list(ex.map(gemm_rows, range(threads)))
                 t3 = time.perf_counter()
                 spent += (t1 - t0) + (t2 - t1b) + (t3 - t2b)
-                total += ((t1 - t0) + (M / 128) * (t2 - t1b) / threads
-                          + (M / (threads * rows_per_thread)) * (t3 - t2b))
+                quant = (t1 - t0) + (M / 128) * (t2 - t1b) / threads
+                gemm = (M / (threads * rows_per_thread)) * (t3 - t2b)
+                total += quant + gemm
+                quant_s += quant
+                gemm_s += gemm
+        single = oracle_single_thread_cases()
         return {"value": self.flops / total / 1e12, "unit": "TFLOP/s", "cores": threads,
-                "kind": "oracle",
+                "kind": "oracle", "cpu_model": cpu_model(),
+                "quantise_s": quant_s, "gemm_s": gemm_s, "single_thread": single,
                 "sample": "per shape: oracle quantise of all of B (%d threads, one slice of "
                           "128-row blocks each) and of one 128-row block of A, then %d full "
                           "output rows of the FP64 dequantised GEMM per thread (%.1f s wall); "
-                          "extrapolated to the full step on the same threads (%.0f s)"
-                          % (threads, rows_per_thread, spent, total)}
+                          "extrapolated to the full step on the same threads (%.0f s: "
+                          "quantise %.1f s, GEMM %.0f s); single_thread: two whole small "
+                          "cases timed on one thread"
+                          % (threads, rows_per_thread, spent, total, quant_s, gemm_s)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_single_thread_cases() -> dict:
+    """The oracle on one thread, whole cases, wall seconds split into
+    quantisation and GEMM: the small single GEMM (128 x 256 x 512, both
+    operands with 128x128 blocks) and one decode GEMM (1 x 24576 x 1536, A
+    with 1x128 blocks, B with 128x128 blocks), seeded normals as in the
+    workloads."""
+    import oracle
+    out = {}
+    for name, (M, N, K, br) in (("small_128x256x512", (128, 256, 512, 128)),
+                                ("decode_1x24576x1536", (1, 24576, 1536, 1))):
+        a = datagen.normal((M, K), 1.0, seed=0, stream=0)
+        b = datagen.normal((N, K), 0.02, seed=0, stream=1)
+        t0 = time.perf_counter()
+        qa, sa = oracle.quantize(a, br)
+        qb, sb = oracle.quantize(b, 128)
+        t1 = time.perf_counter()
+        oracle.gemm_nt(qa, sa, qb, sb, a_block_rows=br)
+        t2 = time.perf_counter()
+        out[name] = {"quantise_s": t1 - t0, "gemm_s": t2 - t1,
+                     "tflops": 2.0 * M * N * K / (t2 - t0) / 1e12}
+    return out
 
 
 class Decode:
@@ -353,6 +395,7 @@ class Decode:
             sb = torch.rand((copies, K // 128, N // 128), device="cuda", generator=g) * 1e-3
             a = torch.from_numpy(datagen.normal((M, K), 1.0, seed=seed, stream=M)).cuda()
             ws_bytes = dg.dg_fp8_gemm_nt_workspace_bytes(M, N, K)
+            a16 = a.to(torch.bfloat16)
             # power-of-two (UE8M0) exponent bytes 120..127, four K blocks per int32
             w = cdiv(K // 128, 4)
             sfa = (torch.randint(120, 128, (w, M, 4), device="cuda", generator=g)
@@ -360,7 +403,7 @@ class Decode:
             sfb = (torch.randint(120, 128, (w, cdiv(N, 128), 4), device="cuda", generator=g)
                    .to(torch.uint8).view(torch.int32).reshape(w, cdiv(N, 128)))
             self.items.append(dict(sfa=sfa, sfb=sfb,
-                M=M, N=N, K=K, qb=qb, sb=sb, a=a, copies=copies,
+                M=M, N=N, K=K, qb=qb, sb=sb, a=a, a16=a16, copies=copies,
                 qa=torch.empty((M, K), dtype=torch.uint8, device="cuda"),
                 sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
                 ws=torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda"),
@@ -378,11 +421,16 @@ class Decode:
         self.dg.dg_fp8_gemm_nt(it["c"], it["qa"], it["qb"][j], it["sa"], it["sb"][j], 1,
                                workspace=it["ws"])
 
+    # rows up to which the step quantises A inside the GEMM: measured faster
+    # than quantiser + GEMM there, slower above (every workgroup then stages
+    # M rows of FP32 A per K block: 4 bytes per value instead of 1)
+    FUSED_STEP_MAX_M = 16
+
     def step(self, i=0):
         # M <= 16: one call quantises A inside the GEMM (same codes and scales);
         # larger M: quantiser, then GEMM
         for it in self.items:
-            if it["M"] <= self.dg.FUSED_A_MAX_M:
+            if it["M"] <= self.FUSED_STEP_MAX_M:
                 self.fused(it, i)
             else:
                 self.quantise_and_gemm(it, i)
@@ -390,14 +438,16 @@ class Decode:
     def outputs(self):
         out = []
         for it in self.items:
-            out += [it["c"]] if it["M"] <= self.dg.FUSED_A_MAX_M else [it["qa"], it["sa"], it["c"]]
+            out += [it["c"]] if it["M"] <= self.FUSED_STEP_MAX_M else [it["qa"], it["sa"], it["c"]]
         return out
 
     def config(self):
         return {"workload": "decode-shaped GEMMs, M in {1,16,64} x (N,K) in {(24576,1536),"
                             "(7168,16384),(4096,4096)}, A 1x128 scales, B 128x128 scales",
-                "step": "quantise A + GEMM per shape (M <= 16: one call that quantises A "
-                        "inside the GEMM); weights rotated over >768 MB of copies"}
+                "step": "quantise A + GEMM per shape (M <= 16: one call that quantises FP32 A "
+                        "inside the GEMM, measured faster there; M = 64: quantiser, then GEMM, "
+                        "measured faster than the fused call); weights rotated over >768 MB "
+                        "of copies"}
 
     def _time_gemm(self, timer, n, it, reps):
         rot = it["copies"]
@@ -413,10 +463,10 @@ class Decode:
         self.dg.dg_quantize_fp8_block(it["qa"], it["sa"], it["a"], 1)
         self.gemm(it, i)
 
-    def fused(self, it, i):
+    def fused(self, it, i, bf16=False):
         j = i % it["copies"]
-        self.dg.dg_fp8_gemm_nt_fused_a(it["c"], it["a"], it["qb"][j], it["sb"][j],
-                                       workspace=it["ws"])
+        self.dg.dg_fp8_gemm_nt_fused_a(it["c"], it["a16"] if bf16 else it["a"], it["qb"][j],
+                                       it["sb"][j], workspace=it["ws"])
 
     def breakdown(self, timer, reps):
         out = []
@@ -433,6 +483,9 @@ class Decode:
             if it["M"] <= self.dg.FUSED_A_MAX_M:
                 row["fused_us"] = timer.time(lambda: [self.fused(it, i) for i in range(rot)],
                                              reps, key=("decf", n)) / rot * 1e3
+                row["fused_bf16_us"] = timer.time(
+                    lambda: [self.fused(it, i, True) for i in range(rot)], reps,
+                    key=("decb", n)) / rot * 1e3
             # the same GEMM with power-of-two (UE8M0) scales on the scaled MFMA
             row["ue8m0_gemm_us"] = timer.time(lambda: [self.gemm_e8(it, i) for i in range(rot)],
                                               reps, key=("dece", n)) / rot * 1e3

@@ -75,6 +75,9 @@ def _load():
     lib.dg_fp8_gemm_nt_fused_a.restype = i32
     lib.dg_fp8_gemm_nt_fused_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t,
                                            vp]
+    lib.dg_fp8_gemm_nt_fused_a_bf16.restype = i32
+    lib.dg_fp8_gemm_nt_fused_a_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp,
+                                                ctypes.c_size_t, vp]
     lib.dg_fp8_grouped_gemm_contig.restype = i32
     lib.dg_fp8_grouped_gemm_contig.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64, i64, vp]
     lib.dg_fp8_grouped_gemm_masked_workspace_bytes.restype = ctypes.c_size_t
@@ -281,14 +284,18 @@ def dg_fp8_gemm_nt_ue8m0(c, a, b, sfa, sfb, a_block_rows: int = 128, workspace=N
                                     _stream(stream)), "dg_fp8_gemm_nt_ue8m0")
 
 
-FUSED_A_MAX_M = 16
+FUSED_A_MAX_M = 64
 
 
 def dg_fp8_gemm_nt_fused_a(c, a, b, sb, workspace=None, stream=None) -> None:
-    """C[M,N] (bf16) = A[M,K] (float32, quantised with 1x128 blocks inside the
-    GEMM) . B[N,K]^T (E4M3, 128x128 scales sb); M <= FUSED_A_MAX_M."""
+    """C[M,N] (bf16) = A[M,K] (float32 or bfloat16, quantised with 1x128
+    blocks inside the GEMM) . B[N,K]^T (E4M3, 128x128 scales sb);
+    M <= FUSED_A_MAX_M."""
     c = _bf16(c, "c")
-    _require(a, torch.float32, "a")
+    if not isinstance(a, torch.Tensor) or a.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("a must be a float32 or bfloat16 tensor")
+    bf16 = a.dtype == torch.bfloat16
+    _require(a, a.dtype, "a")
     b = _codes(b, "b")
     _require(sb, torch.float32, "sb")
     M, K = a.shape
@@ -299,9 +306,9 @@ def dg_fp8_gemm_nt_fused_a(c, a, b, sb, workspace=None, stream=None) -> None:
     if sb.numel() != cdiv(K, 128) * cdiv(N, 128):
         raise ValueError("sb must hold (K/128)*ceil(N/128) floats")
     ws_bytes = _workspace_bytes(workspace)
-    _check(lib.dg_fp8_gemm_nt_fused_a(_ptr(c), _ptr(a), _ptr(b), _ptr(sb), M, N, K,
-                                      _ptr(workspace), ws_bytes, _stream(stream)),
-           "dg_fp8_gemm_nt_fused_a")
+    fn = lib.dg_fp8_gemm_nt_fused_a_bf16 if bf16 else lib.dg_fp8_gemm_nt_fused_a
+    _check(fn(_ptr(c), _ptr(a), _ptr(b), _ptr(sb), M, N, K, _ptr(workspace), ws_bytes,
+              _stream(stream)), "dg_fp8_gemm_nt_fused_a" + ("_bf16" if bf16 else ""))
 
 
 EPILOGUES = {"none": 0, "relu": 1, "silu": 2, "gelu": 3, "swiglu": 4}

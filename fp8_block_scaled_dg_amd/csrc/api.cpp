@@ -167,9 +167,9 @@ int dg_fp8_gemm_nt_ue8m0(uint16_t* c, const uint8_t* a, const uint8_t* b, const 
   return from_hip(dg::launch_gemm_tiled_ue8m0(p, s));
 }
 
-int dg_fp8_gemm_nt_fused_a(uint16_t* c, const float* a, const uint8_t* b, const float* sb,
-                           int64_t M, int64_t N, int64_t K, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+namespace {
+int fused_a(uint16_t* c, const void* a, bool bf16, const uint8_t* b, const float* sb, int64_t M,
+            int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   if (!c || !a || !b || !sb) return DG_ERR_NULL;
   if (M < 1 || M > DG_FUSED_A_MAX_M || N < 8 || K < 128) return DG_ERR_SHAPE;
   if (N % 8 != 0 || K % 128 != 0) return DG_ERR_SHAPE;
@@ -180,8 +180,21 @@ int dg_fp8_gemm_nt_fused_a(uint16_t* c, const float* a, const uint8_t* b, const 
   const int st = check_workspace(M, N, K, &workspace, &workspace_bytes);
   if (st != DG_OK) return st;
   dg::GemmProblem p{c, nullptr, b, nullptr, sb, nullptr, 1, 1, M, N, K};
-  return from_hip(dg::launch_gemm_skinny_fused_a(p, a, workspace, workspace_bytes,
+  return from_hip(dg::launch_gemm_skinny_fused_a(p, a, bf16, workspace, workspace_bytes,
                                                  static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int dg_fp8_gemm_nt_fused_a(uint16_t* c, const float* a, const uint8_t* b, const float* sb,
+                           int64_t M, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return fused_a(c, a, false, b, sb, M, N, K, workspace, workspace_bytes, stream);
+}
+
+int dg_fp8_gemm_nt_fused_a_bf16(uint16_t* c, const uint16_t* a, const uint8_t* b, const float* sb,
+                                int64_t M, int64_t N, int64_t K, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return fused_a(c, a, true, b, sb, M, N, K, workspace, workspace_bytes, stream);
 }
 
 int dg_transpose_fp8(uint8_t* out, const uint8_t* in, int64_t rows, int64_t cols, void* stream) {

@@ -144,6 +144,20 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Maximum over aligned groups of G consecutive lanes (G = 4, 8 or 16): the
+// first two, three or four moves of row16_max.
+template <int G>
+__device__ __forceinline__ float lane_group_max(float v) {
+  static_assert(G == 4 || G == 8 || G == 16, "lane group");
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  if constexpr (G >= 8)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+  if constexpr (G >= 16)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 // ---- fused epilogue (bjdmk.com.cn DeepGEMM page, s3.2: activation and
 // residual applied while the product is in registers; pzsr.cn page, s2.3:
 // SwiGLU), in FP32 before the BF16 rounding ----

@@ -75,10 +75,11 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K);
 bool skinny_applies(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_skinny(const GemmProblem& p, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
-// The same kernel with A given in FP32 (M <= 16) and quantised with 1x128
-// blocks as it is staged; p.a and p.sa are unused.  128-row B tiles.
-hipError_t launch_gemm_skinny_fused_a(const GemmProblem& p, const float* af, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream);
+// The same kernel with A given in FP32 or BF16 (M <= 64) and quantised with
+// 1x128 blocks as it is staged; p.a and p.sa are unused.
+hipError_t launch_gemm_skinny_fused_a(const GemmProblem& p, const void* af, bool bf16,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 // Masked grouped layout on the small-M ring kernel: A [G][max_m][K], C
 // [G][max_m][N], masked_m[g] valid rows per group (device int32, clamped into

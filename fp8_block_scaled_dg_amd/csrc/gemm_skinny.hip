@@ -46,11 +46,15 @@ constexpr int kMaxNS = 8;          // deepest LDS ring (named slot arrays l0 .. 
 constexpr int kMaxCounters = (int)(kSplitkCounterBytes / 4);  // tiles: N up to 1M with 128-row tiles
 constexpr int kMaxSplits = 16;
 
+// Form of the A operand: E4M3 codes with their scales, or FP32 / BF16 values
+// the kernel quantises itself with 1x128 blocks.
+enum AForm { A_CODES = 0, A_F32 = 1, A_BF16 = 2 };
+
 struct SkinnyArgs {
   uint16_t* c;
   Epilogue epi;
   const uint8_t* a;
-  const float* af;  // FP32 A when the kernel quantises A itself, else null
+  const void* af;   // FP32 or BF16 A when the kernel quantises A itself, else null
   const uint32_t* sfa;  // E8: packed UE8M0 exponents (four K blocks per word)
   const uint32_t* sfb;
   const uint8_t* b;
@@ -82,16 +86,19 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
   return r;
 }
 
-// AF32: A arrives as FP32 (M <= 16) and the workgroup quantises it with 1x128
-// blocks: each stage also carries the FP32 A block (16 rows x 128 values,
-// rows past M clamped), fetched by the same LDS DMA as B.  After the step's
-// barrier, thread t encodes values [4j, 4j + 4) and [64 + 4j, 64 + 4j + 4) of
-// row t/16 (j = t%16), the 16 threads of a row share the row's amax through
-// lane exchanges, the codes (in the layout the A DMA produces) and the row
-// scales go to a code buffer, and a second barrier publishes them to the
-// MFMAs.  FP32 A is staged through LDS rather than registers: the compiler
-// waits for every load in flight before using a register loaded ahead of LDS
-// DMA instructions, which would drain the ring each step.
+// AF = A_F32 / A_BF16: A arrives as FP32 or BF16 values and the workgroup
+// quantises it with 1x128 blocks: each stage also carries the A block (MP
+// rows x 128 values, rows past M clamped), fetched by the same LDS DMA as B.
+// After the step's barrier, the TPR = 256 / MP consecutive threads of row
+// t / TPR read its 16-byte chunks j, j + TPR, j + 2 TPR, ... (j = t % TPR),
+// share the row's amax through lane exchanges and encode their values; the
+// codes (in the layout the A DMA produces) and the row scales go to a code
+// buffer, and a second barrier publishes them to the MFMAs.  BF16 values are
+// widened to FP32 exactly, so the codes and scales are those of the FP32
+// quantiser on the widened values.  A is staged through LDS rather than
+// registers: the compiler waits for every load in flight before using a
+// register loaded ahead of LDS DMA instructions, which would drain the ring
+// each step.
 // E8: power-of-two (UE8M0) scales (DeepGEMM page on pzsr.cn, s3.1): the
 // stages carry the packed exponent words in place of the FP32 scales, the
 // scaled MFMA applies them and the accumulators chain through K.
@@ -104,25 +111,31 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
 // (g, chunk, N tile, split) computes rows [chunk * MP, chunk * MP + MP) of
 // group g that are below masked_m[g] (clamped into [0, max_m]), with A, the
 // scales, B and C offset to that group; a chunk with no valid row exits.
-template <int MP, int F, bool AF32 = false, bool E8 = false, int NS = 3, bool MASKED = false>
+template <int MP, int F, int AF = A_CODES, bool E8 = false, int NS = 3, bool MASKED = false>
 __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
-  static_assert(!AF32 || MP == 16, "in-kernel quantisation covers up to 16 rows");
-  static_assert(!(AF32 && E8), "in-kernel quantisation uses FP32 scales");
-  static_assert(!(MASKED && AF32), "masked layout: E4M3 A");
+  constexpr bool AQ = AF != A_CODES;              // A quantised in the kernel
+  static_assert(!(AQ && E8), "in-kernel quantisation uses FP32 scales");
+  static_assert(!(MASKED && AQ), "masked layout: E4M3 A");
+  constexpr int ESZ = AF == A_F32 ? 4 : 2;        // bytes per staged A value (AQ)
+  constexpr int ARB = BK * ESZ;                   // bytes per staged A row (AQ)
+  constexpr int TPR = 256 / MP;                   // quantising threads per A row (AQ)
+  constexpr int CPT = ARB / 16 / TPR;             // 16-byte chunks per thread (AQ)
   constexpr int BNT = 64 * F;                     // B rows per workgroup (F fragments per wave)
   constexpr int MPE = MP < 32 ? 32 : MP;          // A rows staged (>= 4 DMA instructions)
   constexpr int B_BYTES = BNT * BK;               // 8 or 16 KB
-  constexpr int A_BYTES = AF32 ? 16 * BK * 4 : MPE * BK;  // FP32 A (AF32) or E4M3 A
-  constexpr int SA_BYTES = AF32 ? 0 : 4 * 256;    // one 64-float copy per wave
+  constexpr int A_BYTES = AQ ? MP * ARB : MPE * BK;  // FP32 / BF16 A, or E4M3 A
+  constexpr int SA_BYTES = AQ ? 0 : 4 * 256;      // one 64-float copy per wave
   constexpr int SB_BYTES = 4 * 256;               // B block scale (64 copies) per wave
   constexpr int STAGE = B_BYTES + A_BYTES + SA_BYTES + SB_BYTES;
   constexpr int B_IT = B_BYTES / 1024 / 4;        // DMA instructions per wave per stage
   constexpr int A_IT = A_BYTES / 1024 / 4;
-  constexpr int PER_STAGE = B_IT + A_IT + (AF32 ? 1 : 2);  // + the A scale row + the B scale
+  constexpr int PER_STAGE = B_IT + A_IT + (AQ ? 1 : 2);  // + the A scale row + the B scale
   constexpr int NI = MP / 16;                     // A fragments
+  constexpr int QB_BYTES = AQ ? MP * BK + MP * 4 : 16;  // code buffer: codes, then row scales
+  static_assert(!AQ || (A_IT >= 1 && CPT >= 1 && (ARB / 16) % TPR == 0), "A staging");
   static_assert(NS >= 3 && NS <= kMaxNS, "ring depth");
   static_assert((NS - 2) * PER_STAGE <= 63, "s_waitcnt vmcnt range");
-  static_assert(NS * STAGE + (AF32 ? 16 * BK + 16 * 4 : 0) <= 160 * 1024, "LDS");
+  static_assert(NS * STAGE + (AQ ? QB_BYTES : 0) <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t l0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t l1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t l2[STAGE];
@@ -131,9 +144,9 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   __shared__ __attribute__((aligned(1024))) uint8_t l5[NS > 5 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t l6[NS > 6 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t l7[NS > 7 ? STAGE : 16];
-  // AF32 code buffer: 16 rows x 128 codes, then the 16 row scales (never a
-  // DMA target, so stores to it need no wait on the DMA in flight)
-  __shared__ __attribute__((aligned(128))) uint8_t qb[AF32 ? 16 * BK + 16 * 4 : 16];
+  // AQ code buffer: MP rows x 128 codes, then the MP row scales (never a DMA
+  // target, so stores to it need no wait on the DMA in flight)
+  __shared__ __attribute__((aligned(128))) uint8_t qb[QB_BYTES];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
@@ -176,7 +189,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   // 1 KB at LDS offset (j*4 + w)*1024 of the B (or A) region: rows 8*(j*4+w)
   // .. +7, lane L -> row +L/8, physical chunk L%8.
   uint32_t boff[B_IT], aoff[A_IT];
-  const float* a32[AF32 ? A_IT : 1];  // AF32: instruction j's FP32 A row chunk at kb = 0
+  const uint8_t* a32[AQ ? A_IT : 1];  // AQ: instruction j's A row chunk at kb = 0
 #pragma unroll
   for (int j = 0; j < B_IT; ++j) {
     const int r = (j * 4 + wave) * 8 + (lane >> 3);
@@ -186,11 +199,12 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   }
 #pragma unroll
   for (int j = 0; j < A_IT; ++j) {
-    if constexpr (AF32) {
-      // 1 KB = two 512-byte FP32 rows: lane L -> row +L/32, bytes 16*(L%32)
-      const int r = (j * 4 + wave) * 2 + (lane >> 5);
+    if constexpr (AQ) {
+      // 1 KB = 1024 / ARB rows: lane L -> row + L / LPR, bytes 16 (L % LPR)
+      constexpr int LPR = ARB / 16;
+      const int r = (j * 4 + wave) * (64 / LPR) + lane / LPR;
       const int gr = r < p.M ? r : p.M - 1;
-      a32[j] = p.af + (int64_t)gr * p.K + (lane & 31) * 4;
+      a32[j] = static_cast<const uint8_t*>(p.af) + ((int64_t)gr * p.K * ESZ + (lane % LPR) * 16);
       aoff[j] = 0;
     } else {
       const int r = (j * 4 + wave) * 8 + (lane >> 3);
@@ -208,10 +222,10 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
       __builtin_amdgcn_global_load_lds((const void*)(p.b + boff[j] + (uint32_t)kb * BK),
                                        (__attribute__((address_space(3))) void*)(st + (j * 4 + wave) * 1024),
                                        16, 0, 0);
-    if constexpr (AF32) {
+    if constexpr (AQ) {
 #pragma unroll
       for (int j = 0; j < A_IT; ++j)
-        __builtin_amdgcn_global_load_lds((const void*)(a32[j] + (int64_t)kb * BK),
+        __builtin_amdgcn_global_load_lds((const void*)(a32[j] + (int64_t)kb * ARB),
                                          (__attribute__((address_space(3))) void*)(st + B_BYTES + (j * 4 + wave) * 1024),
                                          16, 0, 0);
     } else {
@@ -233,28 +247,50 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
                                      4, 0, 0);
   };
 
-  // in-kernel quantisation of A (AF32): row qr, values [4qj, 4qj + 4) and
-  // [64 + 4qj, 64 + 4qj + 4) of the staged block (conflict-free LDS reads)
-  const int qr = threadIdx.x >> 4;
-  const int qj = threadIdx.x & 15;
+  // in-kernel quantisation of A (AQ): row qr, 16-byte chunks qj + TPR i
+  // (consecutive threads read consecutive chunks: conflict-free)
+  const int qr = threadIdx.x / TPR;
+  const int qj = threadIdx.x % TPR;
   auto quantise_a = [&](const uint8_t* st) {
     // read as integers: a float-typed LDS read makes the compiler wait for
     // every DMA in flight (it cannot tell it from the ring's other slots)
-    const v4i i0 = *reinterpret_cast<const v4i*>(st + B_BYTES + qr * 512 + 16 * qj);
-    const v4i i1 = *reinterpret_cast<const v4i*>(st + B_BYTES + qr * 512 + 256 + 16 * qj);
-    const float4 v0 = make_float4(__int_as_float(i0[0]), __int_as_float(i0[1]),
-                                  __int_as_float(i0[2]), __int_as_float(i0[3]));
-    const float4 v1 = make_float4(__int_as_float(i1[0]), __int_as_float(i1[1]),
-                                  __int_as_float(i1[2]), __int_as_float(i1[3]));
-    const BlockScale bs = block_scale(row16_max(abs_max4(abs_max4(0.0f, v0), v1)));
-    // code byte k of row qr sits in logical 16-byte chunk k/16, at physical
-    // chunk (k/16) ^ swz(qr)
+    v4i raw[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      raw[i] = *reinterpret_cast<const v4i*>(st + B_BYTES + qr * ARB + 16 * (qj + TPR * i));
+    constexpr int NV = CPT * 16 / ESZ / 4;  // float4 groups per thread
+    float4 v[NV];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      if constexpr (AF == A_F32) {
+        v[i] = make_float4(__int_as_float(raw[i][0]), __int_as_float(raw[i][1]),
+                           __int_as_float(raw[i][2]), __int_as_float(raw[i][3]));
+      } else {  // BF16 -> FP32 is exact: the bits move to the top half
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w0 = (uint32_t)raw[i][2 * h], w1 = (uint32_t)raw[i][2 * h + 1];
+          v[2 * i + h] = make_float4(__uint_as_float(w0 << 16), __uint_as_float(w0 & 0xFFFF0000u),
+                                     __uint_as_float(w1 << 16), __uint_as_float(w1 & 0xFFFF0000u));
+        }
+      }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) m = abs_max4(m, v[i]);
+    const BlockScale bs = block_scale(lane_group_max<TPR>(m));
+    // code byte k of row qr sits in logical 16-byte chunk k / 16, at physical
+    // chunk (k / 16) ^ swz(qr); float4 group g of this thread holds values
+    // [4 G, 4 G + 4) of the row with G = its global group index
     const int sw = lds_swz(qr);
-    *reinterpret_cast<uint32_t*>(qb + qr * 128 + (((qj >> 2) ^ sw) * 16) + (qj & 3) * 4) =
-        encode4_block(v0, bs);
-    *reinterpret_cast<uint32_t*>(qb + qr * 128 + ((((qj >> 2) + 4) ^ sw) * 16) + (qj & 3) * 4) =
-        encode4_block(v1, bs);
-    if (qj == 0) reinterpret_cast<float*>(qb + 16 * BK)[qr] = bs.s;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = qj + TPR * (i / (16 / ESZ / 4));  // source chunk of group i
+      const int g = c * (16 / ESZ / 4) + i % (16 / ESZ / 4);
+      const int k = 4 * g;
+      *reinterpret_cast<uint32_t*>(qb + qr * 128 + ((((k >> 4) ^ sw) << 4) | (k & 15))) =
+          encode4_block(v[i], bs);
+    }
+    if (qj == 0) reinterpret_cast<float*>(qb + MP * BK)[qr] = bs.s;
   };
 
   const int fr = lane & 15;
@@ -288,10 +324,10 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   auto body = [&](int it, const uint8_t* cur, uint8_t* nxt) {
     // this wave's loads for stage `it` have landed once at most the loads of
     // the NS-2 younger stages remain outstanding (loads retire in order); with
-    // AF32 its reads of the previous step's codes have completed too
+    // AQ its reads of the previous step's codes have completed too
     // (lgkmcnt 0), so after the barrier the code buffer may be rewritten
     __builtin_amdgcn_s_waitcnt((((NS - 2) * PER_STAGE) & 15) | ((((NS - 2) * PER_STAGE) >> 4) << 14) |
-                               (0x7 << 4) | ((AF32 ? 0x0 : 0xF) << 8));
+                               (0x7 << 4) | ((AQ ? 0x0 : 0xF) << 8));
     // A bare barrier: __syncthreads() adds a workgroup release fence, which
     // waits for every outstanding DMA write to LDS (all NS-1 stages in
     // flight).  Every wave has waited for its own loads of stage `it` above,
@@ -299,7 +335,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
     // so the barrier alone makes stage `it` complete and slot it-1 free.
     asm volatile("s_barrier" ::: "memory");
     issue_stage(it + NS - 1, nxt);
-    if constexpr (AF32) {
+    if constexpr (AQ) {
       quantise_a(cur);
       // the codes are complete (lgkmcnt 0) and visible to every wave
       __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
@@ -320,14 +356,14 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
       for (int i = 0; i < NI; ++i) ea[i] = (int)((w[wave * 64 + 16 * i + fr] >> sh) & 0xFFu);
     } else {
       const float sbv = reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + SA_BYTES)[wave * 64];
-      const float* sa_l = AF32 ? reinterpret_cast<const float*>(qb + 16 * BK)
-                               : reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
+      const float* sa_l = AQ ? reinterpret_cast<const float*>(qb + MP * BK)
+                             : reinterpret_cast<const float*>(cur + B_BYTES + A_BYTES + wave * 256);
 #pragma unroll
       for (int i = 0; i < NI; ++i) s[i] = sa_l[16 * i + fr] * sbv;  // (all 64 slots equal for 128-row A blocks)
     }
     v8i af[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) af[i] = read_frag(AF32 ? qb : cur + B_BYTES, 16 * i, off0, off1);
+    for (int i = 0; i < NI; ++i) af[i] = read_frag(AQ ? qb : cur + B_BYTES, 16 * i, off0, off1);
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const v8i bf = read_frag(cur, wave * 16 * F + 16 * f, off0, off1);
@@ -509,6 +545,18 @@ int choose_bn(int64_t M, int64_t N) {
   return (M > 16 && (N + 127) / 128 < 128 && fits64) ? 64 : 128;
 }
 
+// B rows per workgroup of the kernel that quantises A itself: 128 up to 16
+// rows of A (one 16-row block of FP32 A is small next to 16 KB of B); above
+// that the plain kernel's rule, except FP32 A of more than 32 rows, which
+// takes 64 (with 128 rows its three stages fill all 160 KB of LDS, and the
+// kernel measured 178 us against 22 us for BF16 A at 64 x 24576 x 1536).
+// DG_SKINNY_BN applies here too.
+int fused_bn(int64_t M, int64_t N, bool bf16) {
+  if (M <= 16) return 128;
+  if (M > 32 && !bf16) return (N + 63) / 64 <= kMaxCounters ? 64 : 128;
+  return choose_bn(M, N);
+}
+
 int choose_splits(int64_t M, int64_t N, int64_t K) {
   const int bn = choose_bn(M, N);
   const int64_t tiles = (N + bn - 1) / bn;
@@ -552,8 +600,28 @@ size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return S > 1 ? kSplitkCounterBytes + (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+template <int AF>
+void launch_fused_mp(const SkinnyArgs& p, int mp, int bn, unsigned grid, hipStream_t stream) {
+  if (bn == 64) {
+    if (mp == 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 1, AF>), dim3(grid), dim3(256), 0, stream, p);
+    else if (mp == 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 1, AF>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 1, AF>), dim3(grid), dim3(256), 0, stream, p);
+  } else {
+    if (mp == 16)
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 2, AF>), dim3(grid), dim3(256), 0, stream, p);
+    else if (mp == 32)
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 2, AF>), dim3(grid), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 2, AF>), dim3(grid), dim3(256), 0, stream, p);
+  }
+}
+
+hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const void* af, bool bf16,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
   SkinnyArgs p;
   p.c = q.c; p.a = nullptr; p.af = af; p.b = q.b; p.sa = nullptr; p.sb = q.sb;
   p.sfa = nullptr; p.sfb = nullptr;
@@ -576,8 +644,11 @@ hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const float* af, voi
   p.part_stride = q.M * q.N;
   p.masked_m = nullptr;
   p.max_m = p.chunks = p.tiles = 0;
-  const unsigned grid = (unsigned)(((q.N + 127) / 128) * S);
-  hipLaunchKernelGGL((gemm_skinny_kernel<16, 2, true>), dim3(grid), dim3(256), 0, stream, p);
+  const int mp = q.M <= 16 ? 16 : (q.M <= 32 ? 32 : 64);
+  const int bn = fused_bn(q.M, q.N, bf16);
+  const unsigned grid = (unsigned)(((q.N + bn - 1) / bn) * S);
+  if (bf16) launch_fused_mp<A_BF16>(p, mp, bn, grid, stream);
+  else launch_fused_mp<A_F32>(p, mp, bn, grid, stream);
   return hipGetLastError();
 }
 
@@ -585,18 +656,18 @@ template <bool E8>
 hipError_t launch_mp(const SkinnyArgs& p, int bn, int64_t M, unsigned grid, hipStream_t stream) {
   if (bn == 64) {
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<16, 1, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 1, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
     else if (M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<32, 1, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 1, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<64, 1, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 1, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
   } else {
     if (M <= 16)
-      hipLaunchKernelGGL((gemm_skinny_kernel<16, 2, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_skinny_kernel<16, 2, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
     else if (M <= 32)
-      hipLaunchKernelGGL((gemm_skinny_kernel<32, 2, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_skinny_kernel<32, 2, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<64, 2, false, E8>), dim3(grid), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 2, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -664,10 +735,10 @@ MaskedPlan plan_masked(int num_groups, int64_t max_m, int64_t N, int64_t K) {
 template <int MP, bool E8>
 void launch_masked_mp(const SkinnyArgs& p, int bn, unsigned grid, hipStream_t stream) {
   if (bn == 64)
-    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 1, false, E8, 3, true>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 1, A_CODES, E8, 3, true>), dim3(grid), dim3(256), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 2, false, E8, 3, true>), dim3(grid), dim3(256), 0,
+    hipLaunchKernelGGL((gemm_skinny_kernel<MP, 2, A_CODES, E8, 3, true>), dim3(grid), dim3(256), 0,
                        stream, p);
 }
 

@@ -662,6 +662,17 @@ gemm_ring_kernel(TiledArgs p) {
   }
 }
 
+// Tile rows per band of the dense tile order (see map_tile); DG_GROUP_M
+// overrides it (read once, for tuning sweeps).
+int group_m() {
+  static const int v = [] {
+    const char* e = getenv("DG_GROUP_M");
+    const int g = e ? atoi(e) : 0;
+    return g > 0 ? g : 4;
+  }();
+  return v;
+}
+
 template <bool RING, int A_BLK, bool GROUPED, bool E8 = false, bool KG = false>
 hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   static_assert(!(E8 && RING), "UE8M0 scales: two-stage kernel only");
@@ -678,7 +689,7 @@ hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   p.sb_stride = (int)((q.N + 127) / 128);
   p.tiles_m = GROUPED ? (int)(q.M / 128) : (int)((q.M + 255) / 256);
   p.tiles_n = (int)((q.N + BN - 1) / BN);
-  p.group_m = 4;
+  p.group_m = group_m();
   const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n) * (KG ? (unsigned)q.num_groups : 1u);
   if constexpr (RING)
     hipLaunchKernelGGL((gemm_ring_kernel<A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream, p);

@@ -161,11 +161,14 @@ int dg_fp8_gemm_nt_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
  * inside the GEMM [Q s6: computing the scale factors inside the kernel saves
  * a round trip through global memory; s4.2 for the quantisation]:
  *   c  : out, BF16 [M][N] row-major, 16-byte aligned.
- *   a  : FP32 [M][K] row-major, 16-byte aligned (never written).
+ *   a  : FP32 [M][K] row-major, 16-byte aligned (never written); for
+ *        dg_fp8_gemm_nt_fused_a_bf16, BF16 bit patterns [M][K] (16-byte
+ *        aligned), each widened exactly to FP32 before the quantisation.
  *   b  : E4M3 [N][K] row-major, 16-byte aligned; sb: FP32 [K/128][ceil(N/128)].
- * The result equals dg_quantize_fp8_block(a, block_rows = 1) followed by
- * dg_fp8_gemm_nt(a_block_rows = 1): the codes and scales are the ones the
- * quantiser would write, formed in registers and never stored.
+ * The codes and scales are the ones dg_quantize_fp8_block(a, block_rows = 1)
+ * would write (for the BF16 form: of the widened values), formed on chip and
+ * never stored; the product is then dg_fp8_gemm_nt's (a_block_rows = 1) of
+ * those codes (bit for bit where both run the same kernel plan without split-K).
  *   workspace / workspace_bytes: optional split-K scratch, as for
  *        dg_fp8_gemm_nt (size from dg_fp8_gemm_nt_workspace_bytes(M, N, K);
  *        same workspace rules).
@@ -173,10 +176,13 @@ int dg_fp8_gemm_nt_ue8m0(uint16_t *c, const uint8_t *a, const uint8_t *b,
  * N % 8 == 0; K >= 128, K % 128 == 0; N*K below 2^32; else DG_ERR_SHAPE.
  * Deterministic.
  */
-#define DG_FUSED_A_MAX_M 16
+#define DG_FUSED_A_MAX_M 64
 int dg_fp8_gemm_nt_fused_a(uint16_t *c, const float *a, const uint8_t *b, const float *sb,
                            int64_t M, int64_t N, int64_t K,
                            void *workspace, size_t workspace_bytes, void *stream);
+int dg_fp8_gemm_nt_fused_a_bf16(uint16_t *c, const uint16_t *a, const uint8_t *b,
+                                const float *sb, int64_t M, int64_t N, int64_t K,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * NT GEMM with a fused epilogue [M s3.2: element-wise operators such as the

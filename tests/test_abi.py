@@ -2,6 +2,7 @@
 include/dg.h, and rejects bad arguments on the host before any HIP call
 (these calls enqueue nothing and need no GPU)."""
 import ctypes
+import functools
 import os
 import re
 
@@ -118,25 +119,30 @@ def test_workspace_query_is_host_only(dg):
     assert dg.dg_fp8_gemm_nt_workspace_bytes(0, 4096, 4096) == 0
 
 
-def gf(lib, c=P, a=P, b=P, sb=P, M=16, N=256, K=256, ws=None, wsb=0):
-    return lib.dg_fp8_gemm_nt_fused_a(c, a, b, sb, M, N, K, ws, wsb, None)
+def gf(lib, c=P, a=P, b=P, sb=P, M=16, N=256, K=256, ws=None, wsb=0, bf16=False):
+    fn = lib.dg_fp8_gemm_nt_fused_a_bf16 if bf16 else lib.dg_fp8_gemm_nt_fused_a
+    return fn(c, a, b, sb, M, N, K, ws, wsb, None)
 
 
-def test_fused_a_validation(dg):
+@pytest.mark.parametrize("bf16", [False, True])
+def test_fused_a_validation(dg, bf16):
     lib = dg.lib
+    assert dg.FUSED_A_MAX_M == 64
+    assert gf(lib, M=64, bf16=bf16, a=P1) == 4     # 64 rows pass the shape checks
+    call = functools.partial(gf, bf16=bf16)
     for kw in ("c", "a", "b", "sb"):
-        assert gf(lib, **{kw: None}) == 1
-    assert gf(lib, M=0) == 2
-    assert gf(lib, M=dg.FUSED_A_MAX_M + 1) == 2   # decode batches only
-    assert gf(lib, N=4) == 2
-    assert gf(lib, N=260) == 2            # N % 8
-    assert gf(lib, K=200) == 2            # K % 128
-    assert gf(lib, N=65536, K=65536 + 128) == 2   # N*K >= 2^32
-    assert gf(lib, a=P1) == 4
-    assert gf(lib, sb=ctypes.c_void_p(0x10002)) == 4
+        assert call(lib, **{kw: None}) == 1
+    assert call(lib, M=0) == 2
+    assert call(lib, M=dg.FUSED_A_MAX_M + 1) == 2   # decode batches only
+    assert call(lib, N=4) == 2
+    assert call(lib, N=260) == 2            # N % 8
+    assert call(lib, K=200) == 2            # K % 128
+    assert call(lib, N=65536, K=65536 + 128) == 2   # N*K >= 2^32
+    assert call(lib, a=P1) == 4
+    assert call(lib, sb=ctypes.c_void_p(0x10002)) == 4
     need = dg.dg_fp8_gemm_nt_workspace_bytes(16, 4096, 4096)
-    assert gf(lib, M=16, N=4096, K=4096, ws=P, wsb=16) == 5
-    assert gf(lib, M=16, N=4096, K=4096, ws=P1, wsb=need) == 4
+    assert call(lib, M=16, N=4096, K=4096, ws=P, wsb=16) == 5
+    assert call(lib, M=16, N=4096, K=4096, ws=P1, wsb=need) == 4
 
 
 def test_ue8m0_validation(dg):
