@@ -36,6 +36,7 @@ Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -468,14 +469,48 @@ class Decode:
         self.dg.dg_fp8_gemm_nt_fused_a(it["c"], it["a16"] if bf16 else it["a"], it["qb"][j],
                                        it["sb"][j], workspace=it["ws"])
 
+    def read_probe(self, timer, it, reps):
+        """The weight read alone: the probe kernel reads the same rotated
+        copies of B with 128 bytes per row per K block, 8 KB per wave in
+        flight (no A, no arithmetic); best time over its split counts."""
+        lib = probe_lib()
+        if lib is None:
+            return None
+        N, K = it["N"], it["K"]
+        best = None
+        for splits in (1, 2, 4, 8):
+            if K % (512 * splits):
+                continue
+            out = torch.empty(N // 64 * splits * 256, dtype=torch.int32, device="cuda")
+
+            def one(i, splits=splits, out=out):
+                rc = lib.dgp_hbm_read(it["qb"][i % it["copies"]].data_ptr(), N, K, splits,
+                                      out.data_ptr(),
+                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                if rc != 0:
+                    raise RuntimeError("read probe launch failed (%d)" % rc)
+            rot = it["copies"]
+            t = timer.time(lambda: [one(i) for i in range(rot)], reps,
+                           key=("rdp", N, K, splits)) / rot
+            if best is None or t < best[0]:
+                best = (t, splits)
+        return {"us": best[0] * 1e3, "splits": best[1], "workgroups": N // 64 * best[1],
+                "tbs": N * K / (best[0] * 1e-3) / 1e12}
+
     def breakdown(self, timer, reps):
         out = []
+        probes = {}
         for n, it in enumerate(self.items):
             t = self._time_gemm(timer, n, it, reps)
             b = self.bytes_of(it)
             row = {"mnk": [it["M"], it["N"], it["K"]], "gemm_us": t * 1e3,
                    "hbm_gbs": b / (t * 1e-3) / 1e9,
                    "hbm_frac": b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            key = (it["N"], it["K"])
+            if key not in probes:
+                probes[key] = self.read_probe(timer, it, reps)
+            if probes[key] is not None:
+                row["weight_read_probe"] = probes[key]
             rot = it["copies"]
             row["quantise_gemm_us"] = timer.time(
                 lambda: [self.quantise_and_gemm(it, i) for i in range(rot)], reps,
@@ -868,6 +903,18 @@ def dpm_clocks():
             out["card"] = os.path.basename(os.path.dirname(c))
             return out
     return None
+
+
+def probe_lib():
+    """The measurement probes' own library (not the GEMM library), or None."""
+    path = os.path.join(ROOT, "fp8_block_scaled_dg_amd", "lib", "libdg_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.dgp_hbm_read.restype = ctypes.c_int
+    lib.dgp_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_long, ctypes.c_int,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    return lib
 
 
 def measured_mfma_peak(blocks=1024, iters=10000, reps=3):

@@ -21,7 +21,7 @@ SOURCES = ["quantize.hip", "gemm_tiled.hip", "gemm_skinny.hip", "gemm_stream.hip
            "noalloc.hip", "api.cpp"]
 # measurement probe (its own library; not part of the C ABI in include/dg.h)
 PROBE_LIB = os.path.join(LIBDIR, "libdg_probe.so")
-PROBE_SOURCES = ["probe/peak.hip"]
+PROBE_SOURCES = ["probe/peak.hip", "probe/hbm_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -86,6 +86,134 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
   return r;
 }
 
+// The end of a small-M tile: lane (wave, l) holds acc[f][i] = C[m = 16i + l%16][n = n0 +
+// 16*F*wave + 16f + 4*(l/16) + r], r = 0..3.  Without split-K it stores BF16
+// (with the epilogue); with split-K it publishes its FP32 partial tile, and
+// the last split to arrive sums all S partials in split order and stores.
+template <int MP, int F>
+__device__ __forceinline__ void skinny_finish(const SkinnyArgs& p, const v4f (&acc)[F][MP / 16],
+                                              int tile, int split, int n0, int lane, int wave,
+                                              int& s_last) {
+  constexpr int NI = MP / 16;
+  constexpr int BNT = 64 * F;
+  const int fr = lane & 15;
+  if (p.S == 1) {
+    with_epilogue(p.epi, [&](auto act, auto res) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int m = 16 * i + fr;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
+          if (n < p.N) {
+            const float t[4] = {acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]};
+            store4<decltype(act)::value, decltype(res)::value != 0>(p.c, m, n, t, p.epi);
+          }
+        }
+      }
+    });
+    return;
+  }
+
+  // split-K.  The 8 XCDs have separate L2s, so the partials are published
+  // with device-scope (relaxed atomic) stores, which are written through to
+  // the device-coherent level, and read back with device-scope loads; a full
+  // __threadfence() would instead write back each XCD's whole L2.
+  float* mine = p.partials + (int64_t)split * p.part_stride;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int m = 16 * i + fr;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
+      if (n < p.N) {
+        uint64_t* d = reinterpret_cast<uint64_t*>(mine + (int64_t)m * p.N + n);
+        const uint64_t lo = (uint64_t)__float_as_uint(acc[f][i][0]) |
+                            ((uint64_t)__float_as_uint(acc[f][i][1]) << 32);
+        const uint64_t hi = (uint64_t)__float_as_uint(acc[f][i][2]) |
+                            ((uint64_t)__float_as_uint(acc[f][i][3]) << 32);
+        __hip_atomic_store(d, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(d + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // every store of this wave has completed (is device-visible) ...
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  __syncthreads();  // ... and so have those of every wave of the workgroup
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(&p.counters[tile], 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == p.S - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // The last split sums the S partials in split order (deterministic) and
+  // writes BF16.  Thread t owns the float4 positions t + 256 j of the
+  // M x 128 tile; the loads of G splits x PJ positions are issued together so
+  // that one memory latency covers them, then added in split order.
+  constexpr int PJ = MP * (BNT / 4) / 256;         // positions per thread: 1 .. 8
+  constexpr int G = 16 / PJ;                        // splits loaded per round
+  const int ncols = min(BNT, p.N - n0);
+  float4 sum[PJ];
+  bool live[PJ];
+  int64_t off[PJ];
+  int pm[PJ], pn[PJ];
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    const int idx = threadIdx.x + 256 * j;
+    const int m = idx / (BNT / 4);
+    const int cc = (idx - m * (BNT / 4)) * 4;
+    live[j] = m < p.M && cc < ncols;
+    off[j] = (int64_t)m * p.N + n0 + cc;
+    pm[j] = m;
+    pn[j] = n0 + cc;
+    sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int s0 = 0; s0 < p.S; s0 += G) {
+    uint64_t part[G][PJ][2];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < PJ; ++j) {
+        const int sp = s0 + g;
+        if (sp < p.S && live[j]) {
+          const uint64_t* src =
+              reinterpret_cast<const uint64_t*>(p.partials + (int64_t)sp * p.part_stride + off[j]);
+          part[g][j][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          part[g][j][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < PJ; ++j) {
+        if (s0 + g < p.S && live[j]) {
+          const float4 v = make_float4(__uint_as_float((uint32_t)part[g][j][0]),
+                                       __uint_as_float((uint32_t)(part[g][j][0] >> 32)),
+                                       __uint_as_float((uint32_t)part[g][j][1]),
+                                       __uint_as_float((uint32_t)(part[g][j][1] >> 32)));
+          if (s0 + g == 0) {
+            sum[j] = v;
+          } else {
+            sum[j].x += v.x; sum[j].y += v.y; sum[j].z += v.z; sum[j].w += v.w;
+          }
+        }
+      }
+  }
+  with_epilogue(p.epi, [&](auto act, auto res) {
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) {
+      if (!live[j]) continue;
+      const float t[4] = {sum[j].x, sum[j].y, sum[j].z, sum[j].w};
+      store4<decltype(act)::value, decltype(res)::value != 0>(p.c, pm[j], pn[j], t, p.epi);
+    }
+  });
+  if (threadIdx.x == 0)  // leave the counter zeroed for the next call
+    __hip_atomic_store(&p.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // AF = A_F32 / A_BF16: A arrives as FP32 or BF16 values and the workgroup
 // quantises it with 1x128 blocks: each stage also carries the A block (MP
 // rows x 128 values, rows past M clamped), fetched by the same LDS DMA as B.
@@ -132,7 +260,8 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   constexpr int PER_STAGE = B_IT + A_IT + (AQ ? 1 : 2);  // + the A scale row + the B scale
   constexpr int NI = MP / 16;                     // A fragments
   constexpr int QB_BYTES = AQ ? MP * BK + MP * 4 : 16;  // code buffer: codes, then row scales
-  static_assert(!AQ || (A_IT >= 1 && CPT >= 1 && (ARB / 16) % TPR == 0), "A staging");
+  static_assert(!AQ || (A_IT >= 1 && CPT >= 1 && (ARB / 16) % TPR == 0 && (CPT & (CPT - 1)) == 0),
+                "A staging");
   static_assert(NS >= 3 && NS <= kMaxNS, "ring depth");
   static_assert((NS - 2) * PER_STAGE <= 63, "s_waitcnt vmcnt range");
   static_assert(NS * STAGE + (AQ ? QB_BYTES : 0) <= 160 * 1024, "LDS");
@@ -247,17 +376,24 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
                                      4, 0, 0);
   };
 
-  // in-kernel quantisation of A (AQ): row qr, 16-byte chunks qj + TPR i
-  // (consecutive threads read consecutive chunks: conflict-free)
+  // in-kernel quantisation of A (AQ): row qr, 16-byte chunks
+  // qj + TPR ((i + qr) mod CPT): the TPR threads of a row read consecutive
+  // chunks, and each row starts its rotation at a different group of TPR
+  // chunks, so the rows a wave reads together fall on different LDS banks
+  // (without the rotation the 512-byte FP32 rows of a 64-row block all start
+  // on the same bank: half of the LDS cycles were bank conflicts)
   const int qr = threadIdx.x / TPR;
   const int qj = threadIdx.x % TPR;
+  int qc[CPT];  // chunk read by step i
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) qc[i] = qj + TPR * ((i + qr) & (CPT - 1));
   auto quantise_a = [&](const uint8_t* st) {
     // read as integers: a float-typed LDS read makes the compiler wait for
     // every DMA in flight (it cannot tell it from the ring's other slots)
     v4i raw[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      raw[i] = *reinterpret_cast<const v4i*>(st + B_BYTES + qr * ARB + 16 * (qj + TPR * i));
+      raw[i] = *reinterpret_cast<const v4i*>(st + B_BYTES + qr * ARB + 16 * qc[i]);
     constexpr int NV = CPT * 16 / ESZ / 4;  // float4 groups per thread
     float4 v[NV];
 #pragma unroll
@@ -284,7 +420,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
     const int sw = lds_swz(qr);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c = qj + TPR * (i / (16 / ESZ / 4));  // source chunk of group i
+      const int c = qc[i / (16 / ESZ / 4)];  // source chunk of group i
       const int g = c * (16 / ESZ / 4) + i % (16 / ESZ / 4);
       const int k = 4 * g;
       *reinterpret_cast<uint32_t*>(qb + qr * 128 + ((((k >> 4) ^ sw) << 4) | (k & 15))) =
@@ -401,122 +537,7 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   // drain the re-staged loads past the range before the workgroup exits
   __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
 
-  // lane owns C[m = 16i + l%16][n = n0 + 16*F*wave + 16f + 4*(l/16) + r]
-  if (p.S == 1) {
-    with_epilogue(p.epi, [&](auto act, auto res) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int m = 16 * i + fr;
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int f = 0; f < F; ++f) {
-          const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
-          if (n < p.N) {
-            const float t[4] = {acc[f][i][0], acc[f][i][1], acc[f][i][2], acc[f][i][3]};
-            store4<decltype(act)::value, decltype(res)::value != 0>(p.c, m, n, t, p.epi);
-          }
-        }
-      }
-    });
-    return;
-  }
-
-  // split-K.  The 8 XCDs have separate L2s, so the partials are published
-  // with device-scope (relaxed atomic) stores, which are written through to
-  // the device-coherent level, and read back with device-scope loads; a full
-  // __threadfence() would instead write back each XCD's whole L2.
-  float* mine = p.partials + (int64_t)split * p.part_stride;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int m = 16 * i + fr;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const int n = n0 + wave * 16 * F + 16 * f + 4 * (lane >> 4);
-      if (n < p.N) {
-        uint64_t* d = reinterpret_cast<uint64_t*>(mine + (int64_t)m * p.N + n);
-        const uint64_t lo = (uint64_t)__float_as_uint(acc[f][i][0]) |
-                            ((uint64_t)__float_as_uint(acc[f][i][1]) << 32);
-        const uint64_t hi = (uint64_t)__float_as_uint(acc[f][i][2]) |
-                            ((uint64_t)__float_as_uint(acc[f][i][3]) << 32);
-        __hip_atomic_store(d, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(d + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-  // every store of this wave has completed (is device-visible) ...
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-  __syncthreads();  // ... and so have those of every wave of the workgroup
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(&p.counters[tile], 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == p.S - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // The last split sums the S partials in split order (deterministic) and
-  // writes BF16.  Thread t owns the float4 positions t + 256 j of the
-  // M x 128 tile; the loads of G splits x PJ positions are issued together so
-  // that one memory latency covers them, then added in split order.
-  constexpr int PJ = MP * (BNT / 4) / 256;         // positions per thread: 1 .. 8
-  constexpr int G = 16 / PJ;                        // splits loaded per round
-  const int ncols = min(BNT, p.N - n0);
-  float4 sum[PJ];
-  bool live[PJ];
-  int64_t off[PJ];
-  int pm[PJ], pn[PJ];
-#pragma unroll
-  for (int j = 0; j < PJ; ++j) {
-    const int idx = threadIdx.x + 256 * j;
-    const int m = idx / (BNT / 4);
-    const int cc = (idx - m * (BNT / 4)) * 4;
-    live[j] = m < p.M && cc < ncols;
-    off[j] = (int64_t)m * p.N + n0 + cc;
-    pm[j] = m;
-    pn[j] = n0 + cc;
-    sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  for (int s0 = 0; s0 < p.S; s0 += G) {
-    uint64_t part[G][PJ][2];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < PJ; ++j) {
-        const int sp = s0 + g;
-        if (sp < p.S && live[j]) {
-          const uint64_t* src =
-              reinterpret_cast<const uint64_t*>(p.partials + (int64_t)sp * p.part_stride + off[j]);
-          part[g][j][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          part[g][j][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < PJ; ++j) {
-        if (s0 + g < p.S && live[j]) {
-          const float4 v = make_float4(__uint_as_float((uint32_t)part[g][j][0]),
-                                       __uint_as_float((uint32_t)(part[g][j][0] >> 32)),
-                                       __uint_as_float((uint32_t)part[g][j][1]),
-                                       __uint_as_float((uint32_t)(part[g][j][1] >> 32)));
-          if (s0 + g == 0) {
-            sum[j] = v;
-          } else {
-            sum[j].x += v.x; sum[j].y += v.y; sum[j].z += v.z; sum[j].w += v.w;
-          }
-        }
-      }
-  }
-  with_epilogue(p.epi, [&](auto act, auto res) {
-#pragma unroll
-    for (int j = 0; j < PJ; ++j) {
-      if (!live[j]) continue;
-      const float t[4] = {sum[j].x, sum[j].y, sum[j].z, sum[j].w};
-      store4<decltype(act)::value, decltype(res)::value != 0>(p.c, pm[j], pn[j], t, p.epi);
-    }
-  });
-  if (threadIdx.x == 0)  // leave the counter zeroed for the next call
-    __hip_atomic_store(&p.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  skinny_finish<MP, F>(p, acc, tile, split, n0, lane, wave, s_last);
 }
 
 // Optional override for tuning sweeps: DG_SKINNY_SPLITS=<S> (read once).
