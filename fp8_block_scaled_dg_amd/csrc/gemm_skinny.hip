@@ -673,6 +673,11 @@ hipError_t launch_gemm_skinny_fused_a(const GemmProblem& q, const void* af, bool
   return hipGetLastError();
 }
 
+// Ring depth: 3 slots, except 64-row B tiles with more than 32 rows of A and
+// K >= 4096, where a fourth slot (72 KB of LDS: still two workgroups per CU)
+// measured faster on MI355X (64 x 7168 x 16384: 37.2 against 39.8 us;
+// 64 x 4096 x 4096: 11.9 against 12.1 us; 64 x 24576 x 1536, K = 1536, lost:
+// 14.4 against 13.8 us).
 template <bool E8>
 hipError_t launch_mp(const SkinnyArgs& p, int bn, int64_t M, unsigned grid, hipStream_t stream) {
   if (bn == 64) {
@@ -680,6 +685,8 @@ hipError_t launch_mp(const SkinnyArgs& p, int bn, int64_t M, unsigned grid, hipS
       hipLaunchKernelGGL((gemm_skinny_kernel<16, 1, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
     else if (M <= 32)
       hipLaunchKernelGGL((gemm_skinny_kernel<32, 1, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
+    else if (p.K >= 4096)
+      hipLaunchKernelGGL((gemm_skinny_kernel<64, 1, A_CODES, E8, 4>), dim3(grid), dim3(256), 0, stream, p);
     else
       hipLaunchKernelGGL((gemm_skinny_kernel<64, 1, A_CODES, E8>), dim3(grid), dim3(256), 0, stream, p);
   } else {
