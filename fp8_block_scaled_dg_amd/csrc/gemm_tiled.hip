@@ -65,6 +65,7 @@ struct TiledArgs {
   int sb_stride;  // ceil(N / 128)
   int tiles_m, tiles_n;
   int group_m;
+  int grouped_n_major;  // grouped tile order: N-tile-major instead of row-block-major
 };
 
 __device__ __forceinline__ int lds_swz(int r) { return ((r & 3) << 1) ^ ((r >> 2) & 1); }
@@ -130,9 +131,13 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* lds, int row_base, int o
 // own L2.  The id is first turned into a position L in a tile order such that
 // every XCD gets a contiguous run of L (a bijection for any tile count), then
 // L is mapped to a tile.  Dense: groups of group_m tile-rows swept along N,
-// so concurrently running tiles share A and B panels.  Grouped: N-tile-major,
-// so the tiles that read one expert's B tile (all its row blocks) run back to
-// back on the same XCD and the B tile comes from HBM once.
+// so concurrently running tiles share A and B panels.  Grouped: row-block-
+// major, so an XCD works through all N tiles of two or three 128-row blocks
+// (their A rows stay in its L2) and the row tiles of one expert follow each
+// other, the second pass over the expert's weights finding them in the
+// Infinity Cache.  Measured on MI355X (8 experts, 1024 tokens top-2): up
+// projection 187 -> 159 us, down 159 -> 155 us against the N-tile-major order
+// (p.grouped_n_major, kept for tuning).
 __device__ __forceinline__ void map_tile(const TiledArgs& p, bool grouped, int& tm, int& tn,
                                          int groups = 1, int* kgroup = nullptr) {
   const int bid = blockIdx.x;
@@ -145,8 +150,13 @@ __device__ __forceinline__ void map_tile(const TiledArgs& p, bool grouped, int& 
     L -= *kgroup * per_g;
   }
   if (grouped) {
-    tn = L / p.tiles_m;
-    tm = L - tn * p.tiles_m;
+    if (p.grouped_n_major) {
+      tn = L / p.tiles_m;
+      tm = L - tn * p.tiles_m;
+    } else {
+      tm = L / p.tiles_n;
+      tn = L - tm * p.tiles_n;
+    }
     return;
   }
   const int per_group = p.group_m * p.tiles_n;
@@ -673,6 +683,16 @@ int group_m() {
   return v;
 }
 
+// DG_GROUPED_ORDER=n selects the N-tile-major grouped tile order (read
+// once, for tuning sweeps).
+int grouped_n_major() {
+  static const int v = [] {
+    const char* e = getenv("DG_GROUPED_ORDER");
+    return e && e[0] == 'n' ? 1 : 0;
+  }();
+  return v;
+}
+
 template <bool RING, int A_BLK, bool GROUPED, bool E8 = false, bool KG = false>
 hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   static_assert(!(E8 && RING), "UE8M0 scales: two-stage kernel only");
@@ -690,6 +710,7 @@ hipError_t launch_one(const GemmProblem& q, hipStream_t stream) {
   p.tiles_m = GROUPED ? (int)(q.M / 128) : (int)((q.M + 255) / 256);
   p.tiles_n = (int)((q.N + BN - 1) / BN);
   p.group_m = group_m();
+  p.grouped_n_major = grouped_n_major();
   const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n) * (KG ? (unsigned)q.num_groups : 1u);
   if constexpr (RING)
     hipLaunchKernelGGL((gemm_ring_kernel<A_BLK, GROUPED>), dim3(grid), dim3(512), 0, stream, p);
