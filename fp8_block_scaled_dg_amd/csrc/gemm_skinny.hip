@@ -459,16 +459,19 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs args) {
   // (the slot of stage it-1, free once every wave has passed this barrier)
   auto body = [&](int it, const uint8_t* cur, uint8_t* nxt) {
     // this wave's loads for stage `it` have landed once at most the loads of
-    // the NS-2 younger stages remain outstanding (loads retire in order); with
-    // AQ its reads of the previous step's codes have completed too
-    // (lgkmcnt 0), so after the barrier the code buffer may be rewritten
+    // the NS-2 younger stages remain outstanding (loads retire in order), and
+    // its LDS reads of stage it-1 (and, with AQ, of the previous step's codes)
+    // have returned once lgkmcnt is 0.  The LDS wait is needed: the compiler
+    // moves the MFMAs that consume a step's reads past the next barrier (they
+    // touch only registers), so without it those reads can still be queued
+    // when the DMA below starts refilling their slot.
     __builtin_amdgcn_s_waitcnt((((NS - 2) * PER_STAGE) & 15) | ((((NS - 2) * PER_STAGE) >> 4) << 14) |
-                               (0x7 << 4) | ((AQ ? 0x0 : 0xF) << 8));
+                               (0x7 << 4) | (0x0 << 8));
     // A bare barrier: __syncthreads() adds a workgroup release fence, which
     // waits for every outstanding DMA write to LDS (all NS-1 stages in
-    // flight).  Every wave has waited for its own loads of stage `it` above,
-    // and has consumed its reads of stage it-1 (their results fed the MFMAs),
-    // so the barrier alone makes stage `it` complete and slot it-1 free.
+    // flight).  Every wave has waited for its own loads of stage `it` and its
+    // reads of stage it-1 above, so the barrier alone makes stage `it`
+    // complete and slot it-1 free (and the code buffer rewritable).
     asm volatile("s_barrier" ::: "memory");
     issue_stage(it + NS - 1, nxt);
     if constexpr (AQ) {
