@@ -58,6 +58,20 @@ CSRC = os.path.join(ROOT, "fp8_block_scaled_dg_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 GEMM_TILED_SOURCES = ("gemm_tiled.hip", "dg_device.hpp", "dg_internal.hpp")
+GEMM_SKINNY_SOURCES = ("gemm_skinny.hip", "dg_device.hpp", "dg_internal.hpp")
+
+# Roofline kernels whose HBM traffic is recorded in profiles/traffic.json:
+# config -> (record key, sources hashed into the record, part of the kernel's
+# symbol that the counter rows must carry).
+TRAFFIC_KERNELS = {
+    "dense": ("gemm_tiled_kernel<256,128,false> 8192x8192x8192", GEMM_TILED_SOURCES,
+              "gemm_tiled_kernel<256, 128, false, false, false>"),
+    "decode": ("gemm_skinny_kernel<64,1,codes,false,4> 64x7168x16384", GEMM_SKINNY_SOURCES,
+               "gemm_skinny_kernel<64, 1, 0, false, 4, false>"),
+    "moe": ("gemm_ring_kernel<1,true> grouped up projection 8x11008x4096", GEMM_TILED_SOURCES,
+            "gemm_ring_kernel<1, true>"),
+}
+COPY_BYTES = 1 << 30       # the calibration copy of --config copy
 
 DENSE = [(4096, 7168, 2048), (4096, 4096, 7168), (8192, 8192, 8192)]
 DECODE = [(m, n, k) for (n, k) in [(24576, 1536), (7168, 16384), (4096, 4096)] for m in (1, 16, 64)]
@@ -532,9 +546,12 @@ class Decode:
         t = self._time_gemm(timer, n, it, reps)
         b = self.bytes_of(it)
         ach = b / (t * 1e-3) / 1e9
+        key, src, _ = TRAFFIC_KERNELS["decode"]
+        shape = "%dx%dx%d" % (it["M"], it["N"], it["K"])
         return {"kernel": "decode GEMM %s" % [it["M"], it["N"], it["K"]], "bound": "hbm",
                 "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                "traffic": None, "avg_launch_us": t * 1e3}
+                "traffic": recorded_traffic(key, src) if key.endswith(shape) else None,
+                "algorithmic_bytes": b, "avg_launch_us": t * 1e3}
 
     def cpu_baseline(self):
         return None
@@ -793,9 +810,11 @@ class Moe:
         t = timer.time(lambda: self.gemm(it), reps, key=("moe", 0), calls=4)
         byts = 8 * it["N"] * it["K"] + it["M"] * it["K"] + 2 * it["M"] * it["N"]
         ach = byts / (t * 1e-3) / 1e9
+        key, src, _ = TRAFFIC_KERNELS["moe"]
         return {"kernel": "grouped GEMM up-projection", "bound": "hbm", "achieved": ach,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                "traffic": None, "avg_launch_us": t * 1e3}
+                "traffic": recorded_traffic(key, src), "algorithmic_bytes": byts,
+                "avg_launch_us": t * 1e3}
 
     def cpu_baseline(self):
         return None
@@ -981,6 +1000,86 @@ def run_copy(args):
                       "ms_per_copy": ms, "n_gpus": 1, "steps": args.steps}), flush=True)
 
 
+def pmc_rows(path, counter):
+    """Rows of one counter from a rocprofv3 --pmc CSV (a file, or a directory
+    searched for *counter_collection.csv), in dispatch order."""
+    import csv
+    import glob
+    if os.path.isdir(path):
+        found = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                 recursive=True))
+        if len(found) != 1:
+            raise SystemExit("expected one counter CSV under %s, found %d" % (path, len(found)))
+        path = found[0]
+    with open(path) as f:
+        rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def last_run(rows, symbol):
+    """Counter values of the last run of back-to-back launches of one library
+    kernel (same symbol and grid, no other library kernel in between): under
+    --roofline-only these are exactly the roofline kernel's launches, which
+    come after a separating library launch.  The run's symbol must contain
+    `symbol`."""
+    lib = [r for r in rows if "dg::" in r["Kernel_Name"]]
+    if not lib:
+        raise SystemExit("no library kernel in the counter rows")
+    last = (lib[-1]["Kernel_Name"], lib[-1]["Grid_Size"])
+    if symbol not in last[0]:
+        raise SystemExit("last library kernel is %s, expected %s" % (last[0], symbol))
+    run = []
+    for r in reversed(lib):
+        if (r["Kernel_Name"], r["Grid_Size"]) != last:
+            break
+        run.append(float(r["Counter_Value"]))
+    return last[0], int(last[1]) // int(lib[-1]["Workgroup_Size"]), run
+
+
+def record_traffic(config, pmc_dir):
+    """Write the HBM bytes per launch of `config`'s roofline kernel into
+    profiles/traffic.json, from four rocprofv3 --pmc runs under pmc_dir:
+    <config>_FETCH_SIZE and <config>_WRITE_SIZE of
+    `bench.py --config <config> --roofline-only --kernel-reps 2`, and
+    copy_FETCH_SIZE and copy_WRITE_SIZE of `bench.py --config copy`.  The
+    counters of the copy (COPY_BYTES read, COPY_BYTES written) give the bytes
+    each counter unit stands for; the record carries the hash of the kernel
+    sources, so the bench reports it only while they are unchanged."""
+    key, sources, symbol = TRAFFIC_KERNELS[config]
+    cal = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        v = [float(r["Counter_Value"])
+             for r in pmc_rows(os.path.join(pmc_dir, "copy_" + counter), counter)
+             if "copyBuffer" in r["Kernel_Name"]]
+        if not v or (max(v) - min(v)) > 0.02 * max(v):
+            raise SystemExit("copy calibration for %s: values %s" % (counter, v))
+        cal[counter] = COPY_BYTES / (sum(v) / len(v) * 1024.0)
+    rec = {"source_sha256_16": source_hash(sources)}
+    for counter, what in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        name, wgs, run = last_run(pmc_rows(os.path.join(pmc_dir, "%s_%s" % (config, counter)),
+                                           counter), symbol)
+        if (max(run) - min(run)) > 0.05 * max(run):
+            log("note: %s per dispatch spreads %.1f .. %.1f KiB" % (counter, min(run), max(run)))
+        kib = sum(run) / len(run)
+        rec.update({"kernel": name, "workgroups": wgs,
+                    what + "_dispatches": len(run),
+                    what + "_size_kib_per_dispatch": kib,
+                    what + "_calibration": cal[counter],
+                    what + "_bytes": int(round(kib * 1024.0 * cal[counter]))})
+    rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[key] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    print(json.dumps({key: rec}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -992,7 +1091,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="after the warm-up steps, launch only the roofline kernel (eager, "
+                         "--kernel-reps + 1 times, after one separating library launch) and "
+                         "print its figures: the run that counter passes profile")
+    ap.add_argument("--record-traffic", metavar="PMC_DIR",
+                    help="no GPU: write the roofline kernel's HBM traffic for --config "
+                         "(dense, decode or moe) into profiles/traffic.json from the "
+                         "rocprofv3 --pmc runs under PMC_DIR")
     args = ap.parse_args()
+    if args.record_traffic:
+        if args.config not in TRAFFIC_KERNELS:
+            raise SystemExit("--record-traffic covers %s" % sorted(TRAFFIC_KERNELS))
+        record_traffic(args.config, args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -1038,6 +1150,17 @@ def main():
     for i in range(args.warmup):
         w.step(i)
     torch.cuda.synchronize()
+
+    if args.roofline_only:
+        # a launch of another library kernel separates the warm-up's launches
+        # from the roofline kernel's
+        sep = torch.zeros((16, 16), dtype=torch.uint8, device="cuda")
+        dg.dg_transpose_fp8(torch.empty_like(sep), sep)
+        roof = w.roofline(Timer(False), args.kernel_reps)
+        torch.cuda.synchronize()
+        print(json.dumps({"metric": "roofline kernel alone (eager launches)",
+                          "config": w.config(), "roofline": roof}), flush=True)
+        return
 
     use_graph = not args.no_graph
     timer = Timer(use_graph)
