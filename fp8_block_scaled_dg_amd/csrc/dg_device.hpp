@@ -17,10 +17,18 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Round-to-nearest-even FP32 -> BF16 bits for finite inputs.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two FP32 values rounded to BF16 (nearest, ties to even), packed: a in the
+// low half, b in the high half.  One v_cvt_pk_bf16_f32 on gfx950; an
+// exhaustive sweep of all 2^32 binary32 inputs on the GPU matched the
+// integer rounding (u + 0x7FFF + lsb) >> 16 bit for bit on every finite
+// input, normal and subnormal, and kept NaN a NaN (the integer form can
+// turn a NaN into infinity).  It replaces about ten VALU instructions per
+// pair in every epilogue: staging a 256 x 256 tile through LDS went from
+// ~4.7k to ~2.7k cycles (the conversion had made it VALU-bound).
+typedef float dg_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 dg_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((dg_f2){a, b}, dg_bf16x2));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -223,7 +231,7 @@ __device__ __forceinline__ int epilogue4(int64_t m, int64_t n, const float* t, c
       o0 += bf16_bits_to_f32(r & 0xFFFFu);
       o1 += bf16_bits_to_f32(r >> 16);
     }
-    v.x = bf16_rne(o0) | (bf16_rne(o1) << 16);
+    v.x = bf16x2_rne(o0, o1);
     v.y = 0;
     return 2;
   } else {
@@ -237,8 +245,8 @@ __device__ __forceinline__ int epilogue4(int64_t m, int64_t n, const float* t, c
       o[2] += bf16_bits_to_f32(r.y & 0xFFFFu);
       o[3] += bf16_bits_to_f32(r.y >> 16);
     }
-    v.x = bf16_rne(o[0]) | (bf16_rne(o[1]) << 16);
-    v.y = bf16_rne(o[2]) | (bf16_rne(o[3]) << 16);
+    v.x = bf16x2_rne(o[0], o[1]);
+    v.y = bf16x2_rne(o[2], o[3]);
     return 4;
   }
 }
