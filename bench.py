@@ -1118,7 +1118,7 @@ def main():
         record_traffic(args.config, args.record_traffic)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
