@@ -26,10 +26,16 @@ scaled matrix instruction), --config epilogue (SwiGLU and in-place residual
 fused into the write-back of MLP-shaped GEMMs, against the unfused pair),
 --config wgrad (MoE weight gradient: token-major operands transposed, then
 the K-grouped GEMM), --config masked (decode-time MoE on the masked grouped
-layout: 8 experts with a capacity of 32 rows, 64 tokens top-2), --config copy (a plain device copy of known size, used to calibrate the
+layout: 8 experts with a capacity of 32 rows, 64 tokens top-2), --config
+copy (a plain device copy of known size, used to calibrate the
 FETCH_SIZE/WRITE_SIZE counters), --config peak (the FP8 MFMA-loop probe: the
 matrix-core rate and shader clock this GPU sustains; the dense line also
 carries it as roofline.measured_peak).
+
+Measurement helpers: --roofline-only launches, after the warm-up, only the
+roofline kernel (what rocprofv3 counter passes profile); --record-traffic DIR
+(no GPU) turns the FETCH_SIZE/WRITE_SIZE passes under DIR into the calibrated
+HBM-traffic record in profiles/traffic.json that roofline.traffic reports.
 
 Prints ONE JSON line on stdout.
 """
