@@ -766,6 +766,10 @@ class Moe:
                 sa=torch.empty((K // 128, M), dtype=torch.float32, device="cuda"),
                 c=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
         self.flops = sum(2.0 * self.real_rows * it["N"] * it["K"] for it in self.items)
+        # breakdown only: the balanced grouped call (work shared out by K block
+        # over one workgroup per CU), slower on these weight-streaming shapes
+        self.ws = dg.alloc_workspace(max(dg.dg_fp8_grouped_gemm_contig_workspace_bytes(
+            it["M"], it["N"], it["K"]) for it in self.items))
         # breakdown only: the up projection with gate and up interleaved
         # (2 x 11008 rows per expert) and SwiGLU fused on the write-back
         up = self.items[0]
@@ -775,9 +779,9 @@ class Moe:
             c=torch.empty((M, I), dtype=torch.bfloat16, device="cuda"),
             c_full=torch.empty((M, 2 * I), dtype=torch.bfloat16, device="cuda"), up=up)
 
-    def gemm(self, it):
+    def gemm(self, it, workspace=None):
         self.dg.dg_fp8_grouped_gemm_contig(it["c"], it["qa"], it["qb"], it["sa"], it["sb"], 1,
-                                           it["mi"])
+                                           it["mi"], workspace=workspace)
 
     def glu_fused(self):
         g, up = self.glu, self.glu["up"]
@@ -809,11 +813,12 @@ class Moe:
         out = []
         for n, it in enumerate(self.items):
             t = timer.time(lambda: self.gemm(it), reps, key=("moe", n), calls=4)
+            tb = timer.time(lambda: self.gemm(it, self.ws), reps, key=("moebal", n), calls=4)
             byts = 8 * it["N"] * it["K"] + it["M"] * it["K"] + 2 * it["M"] * it["N"]
             out.append({"nk": [it["N"], it["K"]], "gemm_us": t * 1e3,
                         "tflops_real_rows": 2.0 * self.real_rows * it["N"] * it["K"]
                         / (t * 1e-3) / 1e12,
-                        "hbm_gbs": byts / (t * 1e-3) / 1e9})
+                        "hbm_gbs": byts / (t * 1e-3) / 1e9, "balanced_gemm_us": tb * 1e3})
         up = self.items[0]
         tf = timer.time(self.glu_fused, reps, key=("moeglu", 0), calls=4)
         tu = timer.time(self.glu_unfused, reps, key=("moeglu", 1), calls=4)

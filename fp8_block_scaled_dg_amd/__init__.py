@@ -8,7 +8,7 @@ importing this package raises.
 Entry points (same names as the C ABI):
     dg_quantize_fp8_block(q, scales, x, block_rows)
     dg_fp8_gemm_nt(c, a, b, sa, sb, a_block_rows, workspace=None)
-    dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows, m_indices)
+    dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows, m_indices, workspace=None)
     dg_fp8_grouped_gemm_masked(c, a, b, sa, sb, a_block_rows, masked_m, workspace=None)
     (and the UE8M0, fused-A, epilogue, layout and K-grouped entry points)
 Conveniences mirroring the DeepGEMM page's Python API (pzsr.cn, s4.1):
@@ -26,7 +26,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libdg.so")
 
 DG_OK = 0
-ABI_VERSION = 2
+ABI_VERSION = 3
 # arrival-counter region at the start of every split-K workspace (dg.h)
 WORKSPACE_COUNTER_BYTES = 32768
 
@@ -87,6 +87,11 @@ def _load():
                                                         i64, i32, vp, vp]
     lib.dg_fp8_grouped_gemm_masked_epilogue.restype = i32
     lib.dg_fp8_grouped_gemm_masked_epilogue.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
+                                                        i64, i32, vp, vp, ctypes.c_size_t, vp]
+    lib.dg_fp8_grouped_gemm_contig_workspace_bytes.restype = ctypes.c_size_t
+    lib.dg_fp8_grouped_gemm_contig_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.dg_fp8_grouped_gemm_contig_balanced.restype = i32
+    lib.dg_fp8_grouped_gemm_contig_balanced.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
                                                         i64, i32, vp, vp, ctypes.c_size_t, vp]
     lib.dg_fp8_grouped_gemm_contig_ue8m0.restype = i32
     lib.dg_fp8_grouped_gemm_contig_ue8m0.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i64, i64,
@@ -411,12 +416,19 @@ def dg_fp8_grouped_gemm_k(c, a, b, sa, sb, a_block_rows: int, k_offsets, stream=
            "dg_fp8_grouped_gemm_k")
 
 
+def dg_fp8_grouped_gemm_contig_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib.dg_fp8_grouped_gemm_contig_workspace_bytes(M, N, K)
+
+
 def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices, act: str = "none",
-                               residual=None, stream=None) -> None:
+                               residual=None, workspace=None, stream=None) -> None:
     """Grouped M-contiguous: a [M,K], b [G,N,K], sb [G,K/128,ceil(N/128)],
     m_indices int32 [M] (-1 = padding row -> zero row).  act / residual: the
     fused epilogue (swiglu: each expert's B rows interleave gate and up, c has
-    N/2 columns); padding rows stay zero."""
+    N/2 columns); padding rows stay zero.  workspace (zero-filled device
+    bytes, dg_fp8_grouped_gemm_contig_workspace_bytes(M, N, K) of them; see
+    alloc_workspace): share the work evenly over the compute units
+    (dg_fp8_grouped_gemm_contig_balanced)."""
     c = _bf16(c, "c")
     a = _codes(a, "a")
     b = _codes(b, "b")
@@ -437,7 +449,13 @@ def dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows: int, m_indices, ac
         residual = _bf16(residual, "residual")
         if residual.shape != (M, n_out):
             raise ValueError("residual must be [M, Nout]")
-    if code == 0 and residual is None:
+    if workspace is not None:
+        rc = lib.dg_fp8_grouped_gemm_contig_balanced(_ptr(c), _ptr(a), _ptr(b), _ptr(sa),
+                                                     _ptr(sb), a_block_rows, _ptr(m_indices), G,
+                                                     M, N, K, code, _ptr(residual),
+                                                     _ptr(workspace), _workspace_bytes(workspace),
+                                                     _stream(stream))
+    elif code == 0 and residual is None:
         rc = lib.dg_fp8_grouped_gemm_contig(_ptr(c), _ptr(a), _ptr(b), _ptr(sa), _ptr(sb),
                                             a_block_rows, _ptr(m_indices), G, M, N, K,
                                             _stream(stream))
@@ -573,7 +591,7 @@ def fp8_gemm_nt(c, a, b, sa, sb, a_block_rows: int = 128, workspace=None):
 
 
 def fp8_grouped_gemm_contig(c, a, b, sa, sb, m_indices, a_block_rows: int = 1):
-    dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows, m_indices)
+    dg_fp8_grouped_gemm_contig(c, a, b, sa, sb, a_block_rows, m_indices, workspace=None)
     return c
 
 

@@ -291,6 +291,21 @@ int dg_fp8_grouped_gemm_contig_epilogue(uint16_t* c, const uint8_t* a, const uin
                                         const int32_t* m_indices, int num_groups, int64_t M,
                                         int64_t N, int64_t K, int act, const uint16_t* residual,
                                         void* stream) {
+  return dg_fp8_grouped_gemm_contig_balanced(c, a, b, sa, sb, a_block_rows, m_indices, num_groups,
+                                             M, N, K, act, residual, nullptr, 0, stream);
+}
+
+size_t dg_fp8_grouped_gemm_contig_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 128 || M % 128 != 0 || N < 8 || K < 128 || K % 128 != 0) return 0;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return 0;
+  return dg::grouped_balanced_workspace_bytes(M, N, K);
+}
+
+int dg_fp8_grouped_gemm_contig_balanced(uint16_t* c, const uint8_t* a, const uint8_t* b,
+                                        const float* sa, const float* sb, int a_block_rows,
+                                        const int32_t* m_indices, int num_groups, int64_t M,
+                                        int64_t N, int64_t K, int act, const uint16_t* residual,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_gemm(c, a, b, sa, sb, a_block_rows, M, N, K);
   if (st != DG_OK) return st;
   if (!m_indices) return DG_ERR_NULL;
@@ -300,10 +315,19 @@ int dg_fp8_grouped_gemm_contig_epilogue(uint16_t* c, const uint8_t* a, const uin
   if (residual && !aligned(residual, 16)) return DG_ERR_ALIGN;
   if (M % 128 != 0) return DG_ERR_SHAPE;
   if ((int64_t)num_groups * N * K / num_groups != N * K) return DG_ERR_SHAPE;
+  if (workspace != nullptr && workspace_bytes > 0) {
+    if (workspace_bytes < dg::grouped_balanced_workspace_bytes(M, N, K)) return DG_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DG_ERR_ALIGN;
+  } else {
+    workspace = nullptr;  // one of the two missing: one workgroup per tile
+    workspace_bytes = 0;
+  }
   dg::GemmProblem p{c, a, b, sa, sb, m_indices, num_groups, a_block_rows, M, N, K};
   p.epi.act = act;
   p.epi.res = residual;
-  return from_hip(dg::launch_gemm_tiled(p, true, static_cast<hipStream_t>(stream)));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!workspace) return from_hip(dg::launch_gemm_tiled(p, true, s));
+  return from_hip(dg::launch_gemm_grouped_balanced(p, workspace, workspace_bytes, s));
 }
 
 int dg_fp8_grouped_gemm_contig_ue8m0(uint16_t* c, const uint8_t* a, const uint8_t* b,

@@ -56,6 +56,15 @@ inline Epilogue resolved_epilogue(const GemmProblem& q) {
 
 // Large-tile MFMA kernel (dense or grouped).
 hipError_t launch_gemm_tiled(const GemmProblem& p, bool grouped, hipStream_t stream);
+// Grouped (M-contiguous) GEMM with the (tile, K block) work shared out
+// evenly over one persistent workgroup per CU; pieces of split tiles are
+// summed through the workspace (arrival counters, then partial tiles).  Falls
+// back to launch_gemm_tiled without a large enough workspace or beyond the
+// sizes it applies to.
+bool grouped_balanced_applies(int64_t M, int64_t N, int64_t K);
+size_t grouped_balanced_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_grouped_balanced(const GemmProblem& p, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 // Dense 256 x 256 tile kernel over K groups: C[g] = A[:, Kg] . B[:, Kg]^T.
 hipError_t launch_gemm_tiled_kgrouped(const GemmProblem& p, hipStream_t stream);
 // Dense 256 x 256 tile kernel with UE8M0 scales applied by the scaled MFMA.

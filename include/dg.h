@@ -2,10 +2,11 @@
  * dg.h -- C ABI of the MI355X (gfx950) FP8 block-scaled GEMM library
  * (libdg.so).  C99-compatible; no HIP or PyTorch types appear here.
  *
- * The operations follow two public pages:
+ * The operations follow these public pages:
  *   [Q] "DeepGEMM ... FP8 block-quantised GEMM" (lpnh.cn/news/2826317)
  *   [D] "DeepGEMM: GPU high-efficiency BLAS kernel library" (pzsr.cn/news/21800)
  *   [M] "省算力新利器 DeepGEMM" (bjdmk.com.cn/news/5702840)
+ *   [H] the DeepGEMM tuning walk-through on hotelren.com/news/5487494
  *
  * Conventions for every entry point
  *   - All data pointers are DEVICE pointers owned by the caller; the library
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DG_ABI_VERSION 2
+#define DG_ABI_VERSION 3
 
 /* Size of the arrival-counter region at the start of a split-K workspace. */
 #define DG_WORKSPACE_COUNTER_BYTES 32768
@@ -309,6 +310,37 @@ int dg_fp8_grouped_gemm_contig_epilogue(uint16_t *c, const uint8_t *a, const uin
                                         const int32_t *m_indices, int num_groups, int64_t M,
                                         int64_t N, int64_t K, int act, const uint16_t *residual,
                                         void *stream);
+
+/*
+ * dg_fp8_grouped_gemm_contig_epilogue with the work shared out evenly over
+ * the compute units [D s2.3, s3.2: the grouped MoE GEMM; H s5.6:
+ * persistent workgroups that keep taking work instead of one per tile].  With one workgroup per
+ * 256 x 256 output tile, a launch whose tiles are few next to the compute
+ * units (or a little more than a multiple of them) leaves most of the chip
+ * idle for much of the run.  Here one persistent workgroup per compute unit
+ * takes an equal run of (tile, 128-wide K block) work; a tile split between
+ * workgroups has each piece summed from zero in K order, the FP32 pieces
+ * parked in the workspace, and the last piece to finish adds them in K order
+ * and applies the epilogue.  The result is deterministic (the same bits on
+ * every call for the same inputs and device) and within rounding of the
+ * unsplit call's: the sums of the pieces associate differently.
+ *   workspace / workspace_bytes: device scratch of at least
+ *        dg_fp8_grouped_gemm_contig_workspace_bytes(M, N, K) bytes, 16-byte
+ *        aligned, with the split-K workspace rules given at the top of this
+ *        file (the counter region zero on first use and left zero).  NULL or
+ *        0: this call is dg_fp8_grouped_gemm_contig_epilogue.  A smaller
+ *        non-NULL workspace is DG_ERR_WORKSPACE.
+ * Arguments, requirements and the other errors as
+ * dg_fp8_grouped_gemm_contig_epilogue.  The query returns 0 for shapes the
+ * call does not share out (more than 512 row blocks, or more than 2048
+ * possible tiles): those run one workgroup per tile, workspace or not.
+ */
+size_t dg_fp8_grouped_gemm_contig_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int dg_fp8_grouped_gemm_contig_balanced(uint16_t *c, const uint8_t *a, const uint8_t *b,
+                                        const float *sa, const float *sb, int a_block_rows,
+                                        const int32_t *m_indices, int num_groups, int64_t M,
+                                        int64_t N, int64_t K, int act, const uint16_t *residual,
+                                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Grouped GEMM, experts contiguous along M, with power-of-two (UE8M0) block

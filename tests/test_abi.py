@@ -33,7 +33,9 @@ def test_header_declares_the_boundary():
                  "dg_transpose_fp8", "dg_fp8_gemm", "dg_fp8_gemm_workspace_bytes",
                  "dg_fp8_grouped_gemm_k", "dg_fp8_grouped_gemm_masked",
                  "dg_fp8_grouped_gemm_masked_workspace_bytes", "dg_fp8_grouped_gemm_contig_ue8m0",
-                 "dg_fp8_grouped_gemm_contig_epilogue", "dg_fp8_grouped_gemm_masked_epilogue"):
+                 "dg_fp8_grouped_gemm_contig_epilogue", "dg_fp8_grouped_gemm_masked_epilogue",
+                 "dg_fp8_grouped_gemm_contig_balanced",
+                 "dg_fp8_grouped_gemm_contig_workspace_bytes"):
         assert need in names
 
 
@@ -44,7 +46,7 @@ def test_library_exports_every_declared_symbol(dg):
 
 
 def test_abi_version_and_status_strings(dg):
-    assert dg.lib.dg_abi_version() == 2 == dg.ABI_VERSION
+    assert dg.lib.dg_abi_version() == 3 == dg.ABI_VERSION
     for st in range(0, 8):
         assert dg.status_string(st) and dg.status_string(st) != "unknown status"
     assert dg.status_string(99) == "unknown status"
@@ -244,6 +246,35 @@ def test_grouped_epilogue_validation(dg):
         return lib.dg_fp8_grouped_gemm_masked_epilogue(P, P, P, P, P, 1, MI, 8, 16, 512, 512, act,
                                                        res, None, 0, None)
     assert me(act=7) == 3 and me(res=P1) == 4
+
+
+def test_grouped_balanced_validation(dg):
+    """The balanced grouped GEMM validates like the epilogue call, then its
+    workspace: a too-small one is rejected, a misaligned one too, and none
+    at all means the one-workgroup-per-tile call."""
+    lib = dg.lib
+    MI = ctypes.c_void_p(0x10000)
+
+    def gb(mi=MI, G=8, M=2432, N=4096, K=11008, act=0, res=None, ws=None, wsb=0):
+        return lib.dg_fp8_grouped_gemm_contig_balanced(P, P, P, P, P, 1, mi, G, M, N, K, act, res,
+                                                       ws, wsb, None)
+    assert gb(mi=None) == 1 and gb(G=0) == 3 and gb(act=5) == 3
+    assert gb(M=200) == 2 and gb(K=100) == 2 and gb(res=P1) == 4
+    assert gb(mi=ctypes.c_void_p(0x10002)) == 4
+    need = dg.dg_fp8_grouped_gemm_contig_workspace_bytes(2432, 4096, 11008)
+    # counters, then two partial 256 x 256 FP32 tiles for each of at most 256 workers
+    assert need == dg.WORKSPACE_COUNTER_BYTES + 2 * 256 * 256 * 256 * 4
+    assert gb(ws=P, wsb=need - 1) == 5
+    assert gb(ws=P1, wsb=need) == 4
+    # small problems need fewer slots: 2 row blocks x 1 column tile x 8 K blocks
+    small = dg.dg_fp8_grouped_gemm_contig_workspace_bytes(256, 256, 1024)
+    assert small == dg.WORKSPACE_COUNTER_BYTES + 2 * 4 * 256 * 256 * 4
+    # shapes it does not share out, and invalid ones: no workspace
+    assert dg.dg_fp8_grouped_gemm_contig_workspace_bytes(513 * 128, 256, 1024) == 0
+    assert dg.dg_fp8_grouped_gemm_contig_workspace_bytes(128, 2049 * 256, 1024) == 0
+    assert dg.dg_fp8_grouped_gemm_contig_workspace_bytes(256, 256, 8193 * 128) == 0
+    assert dg.dg_fp8_grouped_gemm_contig_workspace_bytes(200, 256, 1024) == 0
+    assert dg.dg_fp8_grouped_gemm_contig_workspace_bytes(256, 256, 100) == 0
 
 
 def test_grouped_ue8m0_validation(dg):
