@@ -233,3 +233,36 @@ def test_balanced_whole_waves_then_shared(dg, orc):
     pn = np.concatenate([pn, rng.integers(0, N, 1500)])
     ref = sampled_reference(orc, qa, sa, qb, sb, mi, pm, pn, 1)
     assert_close(c[pm, pn], ref, rms=float(np.sqrt(np.mean(ref ** 2))), what="waves")
+
+
+def test_balanced_calls_on_two_streams_with_distinct_workspaces(dg, orc):
+    """Calls are re-entrant: two balanced grouped GEMMs (different shapes)
+    launched again and again on two streams of one GPU, each with its own
+    workspace, give their single-stream bits on every round."""
+    cases = [operands(orc, 100, 2, 256, 1536, 1, seed=51),
+             operands(orc, 300, 2, 384, 768, 128, seed=52, pad_block=True)]
+    brs = [1, 128]
+    wss, eager = [], []
+    for (qa, sa, qb, sb, mi), br in zip(cases, brs):
+        wss.append(workspace(dg, qa.shape[0], qb.shape[1], qa.shape[1]))
+        eager.append(run(dg, qa, sa, qb, sb, mi, br, wss[-1]).view(torch.int16).clone())
+    ref0 = orc.grouped_gemm_contig(*cases[0], a_block_rows=1)
+    real0 = cases[0][4] >= 0
+    assert_close(bf16_to_f64(eager[0].view(torch.bfloat16))[real0], ref0[real0], what="stream case")
+    dev_ops = [tuple(dev(x) for x in ops) for ops in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rnd in range(4):
+        outs = [[torch.full((ops[0].shape[0], ops[2].shape[1]), float("nan"), dtype=torch.bfloat16,
+                            device="cuda") for _ in range(3)] for ops in cases]
+        torch.cuda.synchronize()
+        for j in range(3):                              # interleave the launches
+            for i, st in enumerate(streams):
+                qa, sa, qb, sb, mi = dev_ops[i]
+                with torch.cuda.stream(st):
+                    dg.dg_fp8_grouped_gemm_contig(outs[i][j], qa, qb, sa, sb, brs[i], mi,
+                                                  workspace=wss[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            for o in outs[i]:
+                assert torch.equal(o.view(torch.int16), eager[i]), rnd
+            assert counters_zero(dg, wss[i])
