@@ -313,11 +313,11 @@ int dg_fp8_grouped_gemm_contig_epilogue(uint16_t *c, const uint8_t *a, const uin
 
 /*
  * dg_fp8_grouped_gemm_contig_epilogue with the work shared out evenly over
- * the compute units [D s2.3, s3.2: the grouped MoE GEMM; H s5.6:
- * persistent workgroups that keep taking work instead of one per tile].  With one workgroup per
- * 256 x 256 output tile, a launch whose tiles are few next to the compute
- * units (or a little more than a multiple of them) leaves most of the chip
- * idle for much of the run.  Here one persistent workgroup per compute unit
+ * the compute units [D s2.3, s3.2: the grouped MoE GEMM; H s5.6: persistent
+ * workgroups that keep taking work instead of one per tile].  With one
+ * workgroup per 256 x 256 output tile, a launch whose tiles are few next to
+ * the compute units (or a little more than a multiple of them) leaves much
+ * of the chip idle for part of the run.  Here one persistent workgroup per compute unit
  * takes an equal run of (tile, 128-wide K block) work; a tile split between
  * workgroups has each piece summed from zero in K order, the FP32 pieces
  * parked in the workspace, and the last piece to finish adds them in K order
@@ -332,8 +332,11 @@ int dg_fp8_grouped_gemm_contig_epilogue(uint16_t *c, const uint8_t *a, const uin
  *        non-NULL workspace is DG_ERR_WORKSPACE.
  * Arguments, requirements and the other errors as
  * dg_fp8_grouped_gemm_contig_epilogue.  The query returns 0 for shapes the
- * call does not share out (more than 512 row blocks, or more than 2048
- * possible tiles): those run one workgroup per tile, workspace or not.
+ * call does not share out (more than 512 row blocks, more than 2048
+ * possible tiles, or K above 2^20): those run one workgroup per tile,
+ * workspace or not.  Measured on MI355X it pays where the matrix cores bound
+ * the launch and the last wave of tiles is nearly empty; on MoE shapes bound
+ * by streaming the expert weights the call without a workspace is faster.
  */
 size_t dg_fp8_grouped_gemm_contig_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int dg_fp8_grouped_gemm_contig_balanced(uint16_t *c, const uint8_t *a, const uint8_t *b,
