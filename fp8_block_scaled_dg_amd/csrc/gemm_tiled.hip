@@ -706,12 +706,14 @@ gemm_ring_kernel(TiledArgs p) {
 
 // ---------------------------------------------------------------------------
 // Balanced grouped GEMM.  The grid above gives each workgroup one whole tile;
-// when the tiles are few next to the compute units (the MoE down projection:
-// 176 tiles of 86 K blocks for 256 CUs) most of the chip idles for the whole
-// launch.  Here one persistent workgroup per CU takes an equal share of the
-// (tile, K block) work instead: whole tiles for all but the last one or two
-// waves of tiles, then equal contiguous runs of K blocks over the rest, so a
-// tile may be split between consecutive workgroups at any K block.
+// when the tile count is a little above a multiple of the compute units
+// (288 tiles for 256 CUs) the last wave leaves most of the chip idle.  Here
+// one persistent workgroup per CU takes an equal share of the (tile, K
+// block) work instead: whole tiles for all but the last one or two waves of
+// tiles, then equal contiguous runs of K blocks over the rest, so a tile may
+// be split between consecutive workgroups at any K block.  That pays while
+// the matrix cores bound the launch; where streaming the weights does (the
+// MoE projections), the pieces' extra traffic makes it slower.
 //
 // Every piece of a split tile is summed from zero in K order like a whole
 // tile; each piece's FP32 accumulators go to the workspace, and the last
