@@ -170,6 +170,13 @@ def test_graph_grouped_epilogue_and_ue8m0(dg, orc):
     check_graph(bf16(M, N // 2),
                 lambda o: dg.dg_fp8_grouped_gemm_contig(o[0], A, B, SA, SB, 1, MI, act="swiglu",
                                                         residual=res))
+    # the balanced call: pieces of split tiles pass through the workspace,
+    # whose arrival counters every call leaves zero
+    ws = dg.alloc_workspace(dg.dg_fp8_grouped_gemm_contig_workspace_bytes(M, N, K))
+    check_graph(bf16(M, N // 2),
+                lambda o: dg.dg_fp8_grouped_gemm_contig(o[0], A, B, SA, SB, 1, MI, act="swiglu",
+                                                        residual=res, workspace=ws))
+    assert int(ws[:dg.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
     A8, B8 = dev(qa8), dev(qb8)
     SFA, SFB = dev(orc.pack_ue8m0(ea)), dev(np.stack(sfb))
     check_graph(bf16(M, N),
