@@ -266,3 +266,56 @@ def test_balanced_calls_on_two_streams_with_distinct_workspaces(dg, orc):
             for o in outs[i]:
                 assert torch.equal(o.view(torch.int16), eager[i]), rnd
             assert counters_zero(dg, wss[i])
+
+
+def random_layout(rng, G, max_blocks_per_expert=5):
+    """m_indices for a random contiguous grouped layout: experts in
+    ascending id, each with 0..max_blocks_per_expert 128-row blocks (the
+    last one partly padding), and whole padding blocks here and there."""
+    ids = []
+    for e in range(G):
+        if rng.random() < 0.3:
+            ids += [-1] * 128                      # a whole padding block
+        nb = int(rng.integers(0, max_blocks_per_expert + 1))
+        if nb == 0:
+            continue                               # an expert with no rows
+        real = (nb - 1) * 128 + int(rng.integers(1, 129))
+        ids += [e] * real + [-1] * (nb * 128 - real)
+    if not ids:
+        ids = [0] * 128
+    return np.array(ids, dtype=np.int32)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_layouts_both_grouped_calls(dg, orc, seed):
+    """Random block layouts (runs of 1-5 blocks: pairs and odd 128-row
+    tiles; whole padding blocks; empty experts; up to 9 experts) through the
+    one-workgroup-per-tile call and the balanced call, both against the
+    oracle in full; padding rows must be zeros."""
+    rng = np.random.default_rng(700 + seed)
+    G = int(rng.integers(2, 10))
+    N = int(rng.choice([136, 256, 392, 512]))
+    K = int(rng.choice([256, 640, 1024]))
+    mi = random_layout(rng, G)
+    M = mi.shape[0]
+    a = datagen.normal((M, K), 1.0, seed=700 + seed, stream=1)
+    a[mi < 0] = 0.0
+    br = int(rng.choice([1, 128]))
+    qa, sa = orc.quantize(a, br)
+    w = datagen.normal((G * N, K), 0.02, seed=700 + seed, stream=2)
+    qb = np.empty((G, N, K), np.uint8)
+    sb = np.empty((G, K // 128, (N + 127) // 128), np.float32)
+    for e in range(G):
+        qb[e], sb[e] = orc.quantize(w[e * N:(e + 1) * N], 128)
+    ref = orc.grouped_gemm_contig(qa, sa, qb, sb, mi, a_block_rows=br)
+    real = mi >= 0
+    rms = float(np.sqrt(np.mean(ref[real] ** 2)))
+    nb = dg.dg_fp8_grouped_gemm_contig_workspace_bytes(M, N, K)
+    for ws in (None, dg.alloc_workspace(nb)):
+        c = bf16_to_f64(run(dg, qa, sa, qb, sb, mi, br, ws))
+        what = "layout %d (%s): G %d M %d N %d K %d" % (seed, "balanced" if ws is not None else
+                                                        "per tile", G, M, N, K)
+        assert np.all(c[~real] == 0.0), what
+        assert_close(c[real], ref[real], rms=rms, what=what)
+        if ws is not None:
+            assert counters_zero(dg, ws)
